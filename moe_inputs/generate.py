@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the sparse-MoE layer.
+
+This module is shared by the fp64 oracle and by the GPU path, and it holds no
+arithmetic of the layer itself: it only draws random numbers, scales them to
+the requested standard deviation, rounds them to the storage type and returns
+the stored bit patterns.  Row selection for the routing margin and the Zipf
+bias calibration are computed elsewhere and stored as small tables under
+``tables/`` (see ``tables.py``).
+
+Recipe (all draws are numpy PCG64 streams keyed by
+``SeedSequence([seed, config_id, tensor_id, expert_id])``):
+
+* values are drawn as float32 standard normals, multiplied by the float32
+  standard deviation (one float32 rounding), and for bf16 layers rounded
+  once more to bfloat16 with round-to-nearest-even;
+* x ~ N(0, 1), one stream of rows [T_stream, d];
+* router weight [E, d] ~ N(0, 1/d);
+* per routed expert e: W_up, W_gate [ffn, d] ~ N(0, 1/d), W_down [d, ffn]
+  ~ N(0, 1/ffn); shared experts likewise with ffn_shared;
+* router bias: 'normal' draws float64 N(0, 1) times sqrt(bias_var), stored as
+  float32; 'zipf' is read from the stored table.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import os
+from typing import Dict, Iterator, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .configs import MoEConfig
+
+# stream ids
+X, W_ROUTER, W_UP, W_GATE, W_DOWN, WS_UP, WS_GATE, WS_DOWN, BIAS = range(9)
+
+
+def _rng(cfg: MoEConfig, tensor_id: int, expert_id: int = 0) -> np.random.Generator:
+    ss = np.random.SeedSequence([cfg.seed, cfg.config_id, tensor_id, expert_id])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns.  Inputs are finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _draw(cfg: MoEConfig, tensor_id: int, expert_id: int, shape: Tuple[int, ...],
+          std: float) -> np.ndarray:
+    rng = _rng(cfg, tensor_id, expert_id)
+    z = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    if std != 1.0:
+        z *= np.float32(std)
+    z = z.reshape(shape)
+    if cfg.dtype == "f32":
+        return z
+    return f32_to_bf16_bits(z)
+
+
+def x_stream(cfg: MoEConfig, n_rows: int) -> np.ndarray:
+    """The first ``n_rows`` rows of the token stream, stored type, [n_rows, d].
+    Row i does not depend on n_rows."""
+    return _draw(cfg, X, 0, (n_rows, cfg.d), 1.0)
+
+
+def router_weight(cfg: MoEConfig) -> np.ndarray:
+    return _draw(cfg, W_ROUTER, 0, (cfg.E, cfg.d), 1.0 / np.sqrt(cfg.d))
+
+
+def normal_bias(cfg: MoEConfig) -> np.ndarray:
+    """Per-expert logit bias for the 'normal' recipe, float32 [E]."""
+    z = _rng(cfg, BIAS, 0).standard_normal(cfg.E)
+    return (z * np.sqrt(cfg.bias_var)).astype(np.float32)
+
+
+def expert_weights(cfg: MoEConfig, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(W_up [ffn,d], W_gate [ffn,d], W_down [d,ffn]) of routed expert e."""
+    sd_in, sd_mid = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(cfg.ffn)
+    return (_draw(cfg, W_UP, e, (cfg.ffn, cfg.d), sd_in),
+            _draw(cfg, W_GATE, e, (cfg.ffn, cfg.d), sd_in),
+            _draw(cfg, W_DOWN, e, (cfg.d, cfg.ffn), sd_mid))
+
+
+def shared_weights(cfg: MoEConfig, s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(W_up [ffn_s,d], W_gate [ffn_s,d], W_down [d,ffn_s]) of shared expert s."""
+    sd_in, sd_mid = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(cfg.ffn_shared)
+    return (_draw(cfg, WS_UP, s, (cfg.ffn_shared, cfg.d), sd_in),
+            _draw(cfg, WS_GATE, s, (cfg.ffn_shared, cfg.d), sd_in),
+            _draw(cfg, WS_DOWN, s, (cfg.d, cfg.ffn_shared), sd_mid))
+
+
+def _workers(n: Optional[int]) -> int:
+    if n:
+        return n
+    try:
+        c = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        c = os.cpu_count() or 1
+    return max(1, min(16, c))
+
+
+def iter_experts(cfg: MoEConfig, experts: Sequence[int], shared: bool = False,
+                 workers: Optional[int] = None) -> Iterator[Tuple[int, Tuple[np.ndarray, ...]]]:
+    """Yield (e, weights) for the given expert ids, in order, generating up to
+    ``workers`` experts concurrently (numpy releases the GIL while drawing)."""
+    fn = shared_weights if shared else expert_weights
+    experts = list(experts)
+    w = _workers(workers)
+    with _cf.ThreadPoolExecutor(w) as ex:
+        pending: Dict[int, _cf.Future] = {}
+        nxt = 0
+        for i, e in enumerate(experts):
+            while nxt < len(experts) and nxt < i + 2 * w:
+                pending[nxt] = ex.submit(fn, cfg, experts[nxt])
+                nxt += 1
+            yield e, pending.pop(i).result()
+
+
+def stacked_experts(cfg: MoEConfig, shared: bool = False,
+                    workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """All routed (or shared) expert weights stacked on a leading expert axis."""
+    n = cfg.n_shared if shared else cfg.E
+    f = cfg.ffn_shared if shared else cfg.ffn
+    dt = np.float32 if cfg.dtype == "f32" else np.uint16
+    up = np.empty((n, f, cfg.d), dt)
+    gate = np.empty((n, f, cfg.d), dt)
+    down = np.empty((n, cfg.d, f), dt)
+    for e, (u, g, dn) in iter_experts(cfg, range(n), shared, workers):
+        up[e], gate[e], down[e] = u, g, dn
+    return up, gate, down
+

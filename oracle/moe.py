@@ -1,0 +1,213 @@
+"""The plain fp64 definition of one sparse top-k MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources, cited by page title and section:
+
+* P1 "Mixture of Experts (MoE): routing, expert parallelism, and memory",
+  sections "How does MoE routing work" and "Shared experts".
+* P2 "Mixture of Experts: why a model with 671 billion parameters uses only
+  37", sections "Where MoE changes the Transformer", "The router: how a token
+  chooses experts" (pseudo-PyTorch layer) and "Shared expert and fine-grained
+  experts".
+* P3 "Mixture of experts: how MoE works and what it costs", sections "What
+  mixture of experts costs in compute" and "How batching changes the mixture
+  of experts math" (occupancy closed form).
+* P4 "Mixture of Experts Explained: Routers, Active Parameters and VRAM", the
+  five numbered routing steps (Score, Normalise, Keep the top k, Renormalise,
+  Run and combine), the gated three-matrix feed-forward remark, the worked
+  example and "Softmax before or after the top-k step".
+
+Readings where the pages leave a step open (each is also listed in the design
+notes of the repository):
+
+* the gated expert is SwiGLU: h = SiLU(x W_gate^T) * (x W_up^T), out = h W_down^T,
+  with SiLU(z) = z / (1 + exp(-z)) and no biases;
+* selection keeps the k largest logits in descending order; an exact tie goes
+  to the lower expert index; selection is done on logits (softmax is monotone,
+  so the chosen set and order are the same as on probabilities);
+* the kept probabilities are renormalised to sum to one (P4 step 4);
+* a per-expert bias, when present, is added to the logits before the softmax;
+* shared experts are added with coefficient one; no residual term is added.
+
+Parity status: every function here is pinned by a CPU test against the pages'
+printed worked example, closed forms, brute force or a library routine, except
+the Zipf bias calibration in ``make_input_tables.py``, whose outcome is an
+input recipe and is parity unpinned.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64, exactly.  'bf16' storage is the upper 16 bits
+    of an IEEE float32, so shifting the pattern left by 16 gives the float32
+    with the same value."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """P1 "How does MoE routing work" step 1, P2 "The router", P4 step
+    "Score": one score per expert = token hidden state times the E x d router
+    matrix (a bias-free linear layer).  The optional per-expert bias is added
+    here.  x [T,d] f64, w_router [E,d] f64 -> logits [T,E] f64."""
+    L = x @ w_router.T
+    if bias is not None:
+        L = L + np.asarray(bias, np.float64)[None, :]
+    return L
+
+
+def softmax(L: np.ndarray) -> np.ndarray:
+    """P4 step "Normalise": probabilities over all E experts, summing to 1."""
+    m = L.max(axis=-1, keepdims=True)
+    e = np.exp(L - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def select_topk(L: np.ndarray, k: int) -> np.ndarray:
+    """P4 step "Keep the top k": the k largest scores of each token, in
+    descending order; an exact tie goes to the lower expert index.  Returns
+    int32 [T,k]."""
+    T, E = L.shape
+    e_ix = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((e_ix, -L), axis=-1)  # primary: -L ascending; then e
+    return order[:, :k].astype(np.int32)
+
+
+def renormalise(P: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """P4 step "Renormalise": divide the k kept probabilities by their sum."""
+    kept = np.take_along_axis(P, idx.astype(np.int64), axis=-1)
+    return kept / kept.sum(axis=-1, keepdims=True)
+
+
+def route(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int):
+    """Router: logits, probabilities, top-k indices and renormalised weights."""
+    L = router_logits(x, w_router, bias)
+    P = softmax(L)
+    idx = select_topk(L, k)
+    w = renormalise(P, idx)
+    return L, P, idx, w
+
+
+def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
+    """Tokens per expert: how many (token, slot) pairs chose each expert (the
+    per-expert count printed in the P4 worked example).  int32 [E]."""
+    flat = np.asarray(idx).ravel()
+    return np.array([int(np.sum(flat == e)) for e in range(E)], dtype=np.int32)
+
+
+def dispatch_order(idx: np.ndarray, E: int) -> np.ndarray:
+    """Grouping of (token, slot) pairs by expert (P2 "The router" pseudo-layer
+    loops experts and gathers the tokens that chose each; P3 "What mixture of
+    experts costs in compute": tokens are grouped by expert before each
+    multiply).  Returns the flat pair ids t*k+j, expert 0's first, each
+    expert's pairs in increasing pair id."""
+    flat = np.asarray(idx).ravel()
+    parts = [np.nonzero(flat == e)[0] for e in range(E)]
+    return (np.concatenate(parts) if parts else np.zeros(0, np.int64)).astype(np.int64)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(X: np.ndarray, w_up: np.ndarray, w_gate: np.ndarray,
+                  w_down: np.ndarray) -> np.ndarray:
+    """One gated expert FFN (P4: a gated block with three matrices; P2 "Where
+    MoE changes the Transformer": two linear layers with an activation between
+    them): SiLU(X W_gate^T) * (X W_up^T), then times W_down^T.
+    X [n,d]; w_up, w_gate [f,d]; w_down [d,f] -> [n,d]."""
+    U = X @ w_up.T
+    G = X @ w_gate.T
+    return (silu(G) * U) @ w_down.T
+
+
+def topk_gaps(L: np.ndarray, k: int) -> np.ndarray:
+    """Smallest gap between consecutive logits among the k+1 largest of each
+    token (the k largest when k equals E).  A token whose gap is at least a
+    margin m has a top-k set and order that any logit error below m/2 cannot
+    change."""
+    T, E = L.shape
+    s = -np.sort(-L, axis=-1)[:, :min(k + 1, E)]
+    if s.shape[1] < 2:
+        return np.full(T, np.inf)
+    return np.min(s[:, :-1] - s[:, 1:], axis=-1)
+
+
+def share_touched(k: int, E: int, B: int) -> float:
+    """P3 "How batching changes the mixture of experts math": expected share
+    of the E experts used by at least one of B tokens when each token picks k
+    distinct experts uniformly at random: 1 - (1 - k/E)^B."""
+    return 1.0 - (1.0 - k / E) ** B
+
+
+@dataclass
+class MoEResult:
+    y: np.ndarray          # [n_tokens, d] float64 (rows of `tokens`)
+    idx: np.ndarray        # [T, k] int32
+    w: np.ndarray          # [T, k] float64
+    counts: np.ndarray     # [E] int32
+    logits: np.ndarray     # [T, E] float64
+    probs: np.ndarray      # [T, E] float64
+    tokens: np.ndarray     # token ids y covers
+
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int,
+                expert_fn: ExpertFn, E: int, dtype: str,
+                shared_fn: Optional[ExpertFn] = None, n_shared: int = 0,
+                tokens: Optional[Sequence[int]] = None) -> MoEResult:
+    """The whole layer (P4 step "Run and combine"; P1 "Shared experts"):
+
+        y[t] = sum_{j<k} w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])
+
+    summed in slot order j = 0..k-1, then the shared experts.  Only the
+    experts that some token chose are evaluated, each on just its tokens.
+
+    x and w_router are stored arrays (``dtype`` 'f32' or 'bf16' bit patterns);
+    expert_fn(e) / shared_fn(s) return the stored (W_up, W_gate, W_down) of an
+    expert.  Routing is computed for all T tokens; y only for ``tokens``
+    (default: all), so large layers can be checked on a sample.
+    """
+    X = widen(x, dtype)
+    L, P, idx, w = route(X, widen(w_router, dtype), bias, k)
+    T = X.shape[0]
+    counts = expert_counts(idx, E)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    # per (sampled token, slot) expert output, then a slot-ordered sum
+    slot_out = np.zeros((len(tok), k, X.shape[1]))
+    order = dispatch_order(idx[tok], E)
+    sub_idx = idx[tok].ravel()
+    start = 0
+    for e in range(E):
+        n_e = int(np.sum(sub_idx == e))
+        if n_e == 0:
+            continue
+        pairs = order[start:start + n_e]
+        start += n_e
+        rows = pairs // k
+        wu, wg, wd = (widen(a, dtype) for a in expert_fn(e))
+        out = swiglu_expert(X[tok[rows]], wu, wg, wd)
+        slot_out[rows, pairs % k] = out
+    y = np.zeros((len(tok), X.shape[1]))
+    wt = w[tok]
+    for j in range(k):
+        y += wt[:, j:j + 1] * slot_out[:, j]
+    for s in range(n_shared):
+        su, sg, sd = (widen(a, dtype) for a in shared_fn(s))
+        y += swiglu_expert(X[tok], su, sg, sd)
+    return MoEResult(y, idx, w, counts, L, P, tok)

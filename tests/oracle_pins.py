@@ -1,0 +1,251 @@
+"""Checks that tie the fp64 oracle to facts fixed by the source pages and by
+mathematics, independently of the oracle's own code.  Each check raises
+AssertionError on a mismatch; ``test_oracle_pins.py`` runs them and
+``test_oracle_mutations.py`` plants mistakes in the oracle to show that each
+check notices.
+
+Independent means: the expected values come from the pages' printed numbers,
+from closed forms, from brute force over all k-subsets / all experts, or from
+library routines (torch.nn.functional, scipy.special), never from re-running
+the oracle's formula.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle.moe as om
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- worked example
+def worked_example_inputs():
+    """The page's toy layer, built with torch's seeded init in the page's order
+    (router, then each expert's two linear layers, then the tokens)."""
+    g = golden("worked_example_routing.json")["model"]
+    torch.manual_seed(g["seed"])
+    router = torch.nn.Linear(g["d_model"], g["num_experts"], bias=False)
+    experts = []
+    for _ in range(g["num_experts"]):
+        up = torch.nn.Linear(g["d_model"], g["d_ff"], bias=False)
+        down = torch.nn.Linear(g["d_ff"], g["d_model"], bias=False)
+        experts.append((up, down))
+    x = torch.randn(g["tokens"], g["d_model"])
+    return (x.double().numpy(), router.weight.detach().double().numpy(), experts, g)
+
+
+def check_worked_example_routing():
+    """Pins router logits, softmax, top-k and counts on the page's own inputs
+    (P4 worked example: first token's experts, tokens per expert, experts
+    touched by growing prefixes, balance loss, capacity drop)."""
+    G = golden("worked_example_routing.json")
+    x, wr, _, g = worked_example_inputs()
+    L, P, idx, w = om.route(x, wr, None, g["k"])
+    assert idx[0].tolist() == G["first_token_experts"], idx[0]
+    counts = om.expert_counts(idx, g["num_experts"])
+    assert counts.tolist() == G["tokens_per_expert"], counts
+    for n, touched in G["experts_touched_after_tokens"].items():
+        c = om.expert_counts(idx[: int(n)], g["num_experts"])
+        assert int(np.sum(c > 0)) == touched, (n, c)
+    f = counts / counts.sum()
+    loss = g["num_experts"] * float(np.sum(f * P.mean(axis=0)))
+    assert round(loss, 4) == G["balance_loss_rounded_4"], loss
+    cap = math.ceil(g["tokens"] * g["k"] / g["num_experts"] * 1.25)
+    assert int(np.clip(counts - cap, 0, None).sum()) == G["capacity_factor_1_25_dropped"]
+    # P4 "Softmax before or after the top-k step": softmax over the kept logits
+    kept = np.take_along_axis(L, idx.astype(np.int64), axis=1)
+    w2 = scipy.special.softmax(kept, axis=1)
+    assert np.max(np.abs(w2 - w)) < 1e-14
+    assert np.max(np.abs(w2 - w)) < G["softmax_order_max_difference_below"]
+
+
+# ---------------------------------------------------------------- random layers
+def rand_layer(seed, T, d, E, k, f, n_shared=0, f_sh=0, bias=True, square=False):
+    rng = np.random.default_rng(seed)
+    if square:
+        f = d
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / np.sqrt(d)
+    b = rng.standard_normal(E) * 0.7 if bias else None
+    ex = [(rng.standard_normal((f, d)) / np.sqrt(d), rng.standard_normal((f, d)) / np.sqrt(d),
+           rng.standard_normal((d, f)) / np.sqrt(f)) for _ in range(E)]
+    sh = [(rng.standard_normal((f_sh, d)) / np.sqrt(d), rng.standard_normal((f_sh, d)) / np.sqrt(d),
+           rng.standard_normal((d, f_sh)) / np.sqrt(f_sh)) for _ in range(n_shared)]
+    return x, wr, b, ex, sh
+
+
+def torch_ffn(xrow, wu, wg, wd):
+    """SwiGLU expert with library routines (torch fp64 CPU)."""
+    X = torch.from_numpy(np.atleast_2d(xrow))
+    h = F.silu(F.linear(X, torch.from_numpy(wg))) * F.linear(X, torch.from_numpy(wu))
+    return F.linear(h, torch.from_numpy(wd)).numpy()
+
+
+def brute_force_y(x, wr, b, ex, sh, k):
+    """Dense evaluation (P4: the loop matched a slow version that runs every
+    expert with zero weight for the unpicked ones): every token through every
+    expert, gated by a length-E vector that is zero off the top-k.  The top-k
+    set is the k-subset with the largest logit sum, over all subsets; the
+    weights are library softmax probabilities renormalised over that set."""
+    T, d = x.shape
+    E = wr.shape[0]
+    L = x @ wr.T + (0 if b is None else b)
+    P = scipy.special.softmax(L, axis=1)
+    y = np.zeros((T, d))
+    for t in range(T):
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(L[t, list(s)]))
+        gate = np.zeros(E)
+        gate[list(best)] = P[t, list(best)] / P[t, list(best)].sum()
+        for e in range(E):
+            y[t] += gate[e] * torch_ffn(x[t], *ex[e])[0]
+        for s in sh:
+            y[t] += torch_ffn(x[t], *s)[0]
+    return y
+
+
+def run_oracle_f64(x, wr, b, ex, sh, k):
+    """Call the oracle on float64 arrays (store them as 'f32' is not exact, so
+    pass fp64 straight through widen's f32 branch, which is astype(float64))."""
+    return om.moe_forward(x, wr, b, k, lambda e: ex[e], wr.shape[0], "f32",
+                          (lambda s: sh[s]) if sh else None, len(sh))
+
+
+def check_brute_force(seed=1, T=24, d=16, E=6, k=3, f=20, n_shared=1, square=False):
+    x, wr, b, ex, sh = rand_layer(seed, T, d, E, k, f, n_shared, f, square=square)
+    r = run_oracle_f64(x, wr, b, ex, sh, k)
+    yb = brute_force_y(x, wr, b, ex, sh, k)
+    err = np.max(np.abs(r.y - yb)) / np.sqrt(np.mean(yb ** 2))
+    assert err < 1e-12, err
+
+
+def check_topk_bruteforce(seed=2, T=200, E=7, k=3):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E))
+    idx = om.select_topk(L, k)
+    for t in range(T):
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(L[t, list(s)]))
+        assert set(idx[t].tolist()) == set(best)
+        vals = L[t, idx[t]]
+        assert np.all(vals[:-1] > vals[1:])
+
+
+def check_tie_break():
+    """Exact ties go to the lower expert index (the layer's stated tie rule)."""
+    L = np.array([[0.5, 0.7, 0.7, 0.1],
+                  [0.7, 0.5, 0.7, 0.7],
+                  [0.0, 0.0, 0.0, 0.0],
+                  [-1.0, 2.0, -1.0, 2.0]])
+    assert om.select_topk(L, 2).tolist() == [[1, 2], [0, 2], [0, 1], [1, 3]]
+    assert om.select_topk(L, 1).tolist() == [[1], [0], [0], [1]]
+    assert om.select_topk(L, 4)[2].tolist() == [0, 1, 2, 3]
+
+
+def check_softmax_library(seed=3):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((50, 33)) * 4
+    assert np.max(np.abs(om.softmax(L) - scipy.special.softmax(L, axis=1))) < 1e-15
+
+
+def check_invariants(seed=4, T=300, E=16, k=4):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, 24))
+    wr = rng.standard_normal((E, 24))
+    L, P, idx, w = om.route(x, wr, rng.standard_normal(E), k)
+    assert np.max(np.abs(w.sum(axis=1) - 1)) < 1e-14
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == k
+        assert np.all(np.diff(L[t, idx[t]]) < 0)
+    counts = om.expert_counts(idx, E)
+    assert counts.sum() == T * k
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    order = om.dispatch_order(idx, E)
+    assert np.array_equal(order, np.argsort(idx.ravel(), kind="stable"))
+    # k = 1: renormalised weight is exactly one (P4 "Why top-1 routing cannot renormalise")
+    _, _, _, w1 = om.route(x, wr, None, 1)
+    assert np.all(w1 == 1.0)
+
+
+def check_uniform_gates():
+    """All-zero router: every logit ties, so with k = E each weight is 1/E and
+    y is the mean of all experts; with k < E it is the mean of experts 0..k-1."""
+    rng = np.random.default_rng(5)
+    T, d, E, f = 6, 12, 5, 10
+    x, _, _, ex, _ = rand_layer(5, T, d, E, E, f, bias=False)
+    wr = np.zeros((E, d))
+    for k in (E, 2):
+        r = run_oracle_f64(x, wr, None, ex, [], k)
+        ref = np.mean([torch_ffn(x, *ex[e]) for e in range(k)], axis=0)
+        assert np.max(np.abs(r.y - ref)) < 1e-13, k
+        assert np.all(r.idx == np.arange(k)[None, :])
+    del rng
+
+
+def check_single_expert_library():
+    """E = 1, k = 1 reduces to one dense SwiGLU FFN (torch library)."""
+    x, wr, _, ex, _ = rand_layer(6, 9, 16, 1, 1, 24, bias=False)
+    r = run_oracle_f64(x, wr, None, ex, [], 1)
+    assert np.max(np.abs(r.y - torch_ffn(x, *ex[0]))) < 1e-13
+
+
+def check_silu():
+    z = np.linspace(-30, 30, 601)
+    assert np.max(np.abs(om.silu(z) - F.silu(torch.from_numpy(z)).numpy())) < 1e-14
+    # z*s(z) - (-z)*s(-z) = z, since s(z) + s(-z) = 1
+    assert np.max(np.abs(om.silu(z) - om.silu(-z) - z)) < 1e-12
+    assert om.silu(np.array([0.0]))[0] == 0.0
+
+
+def check_widen():
+    vals = torch.randn(1000, dtype=torch.float32) * 3
+    b = vals.to(torch.bfloat16)
+    bits = b.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(om.widen(bits, "bf16"), b.double().numpy())
+
+
+def check_occupancy_table():
+    G = golden("occupancy_table.json")
+    for key, row in G["share_touched_percent_1dp"].items():
+        parts = key.split("_")
+        k, E = int(parts[1][1:]), int(parts[2][1:])
+        for B, pct in zip(G["batches"], row):
+            assert round(100 * om.share_touched(k, E, B), 1) == pct, (key, B)
+    M = G["mixtral_weights_read"]
+    expert_B = (M["total_params_B"] - M["active_params_B"]) / (1 - M["k"] / M["E"])
+    other_B = M["total_params_B"] - expert_B
+    for B, pct, wread in zip(M["batches"], M["experts_touched_percent"], M["weights_read_B"]):
+        s = om.share_touched(M["k"], M["E"], B)
+        assert round(100 * s, 1) == pct
+        assert abs(other_B + s * expert_B - wread) <= 0.1 + 1e-9, (B, other_B + s * expert_B)
+
+
+def check_occupancy_monte_carlo(trials=3000, seed=7):
+    """Routing with iid logits is uniform over k-subsets, so the mean touched
+    share matches the closed form (P3: a Monte Carlo run agreed within 0.05
+    percentage points)."""
+    rng = np.random.default_rng(seed)
+    for k, E, B in ((2, 8, 4), (8, 256, 16), (4, 128, 8)):
+        shares = np.empty(trials)
+        for i in range(trials):
+            idx = om.select_topk(rng.standard_normal((B, E)), k)
+            shares[i] = np.sum(om.expert_counts(idx, E) > 0) / E
+        se = shares.std() / np.sqrt(trials)
+        assert abs(shares.mean() - om.share_touched(k, E, B)) < 4 * se + 1e-12, (k, E, B)
+
+
+ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, check_tie_break,
+       check_softmax_library, check_invariants, check_uniform_gates,
+       check_single_expert_library, check_silu, check_widen, check_occupancy_table,
+       check_occupancy_monte_carlo]

@@ -1,0 +1,83 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by a pin.
+
+Each case swaps one oracle function for a plausible wrong version and checks
+that at least the named pin fails."""
+import numpy as np
+import pytest
+
+import oracle.moe as om
+import oracle_pins as P
+
+
+def _ties_to_high(L, k):
+    T, E = L.shape
+    e_ix = np.broadcast_to(-np.arange(E), (T, E))
+    return np.lexsort((e_ix, -L), axis=-1)[:, :k].astype(np.int32)
+
+
+def _no_renorm(Pm, idx):
+    return np.take_along_axis(Pm, idx.astype(np.int64), axis=-1)
+
+
+def _swapped_swiglu(X, wu, wg, wd):
+    return (om.silu(X @ wu.T) * (X @ wg.T)) @ wd.T
+
+
+def _transposed_down(X, wu, wg, wd):
+    return (om.silu(X @ wg.T) * (X @ wu.T)) @ wd
+
+
+def _no_bias(x, w, bias=None):
+    return x @ w.T
+
+
+def _sign_silu(z):
+    return z / (1.0 + np.exp(z))
+
+
+def _ascending(L, k):
+    T, E = L.shape
+    e_ix = np.broadcast_to(np.arange(E), (T, E))
+    return np.lexsort((e_ix, L), axis=-1)[:, :k].astype(np.int32)
+
+
+def _counts_off_by_one(idx, E):
+    flat = np.asarray(idx).ravel()
+    return np.array([int(np.sum(flat == e + 1)) for e in range(E)], dtype=np.int32)
+
+
+def _unstable_order(idx, E):
+    return np.argsort(np.asarray(idx).ravel(), kind="quicksort")[::-1].astype(np.int64)
+
+
+MUTANTS = [
+    ("select_topk", _ties_to_high, P.check_tie_break),
+    ("select_topk", _ascending, P.check_worked_example_routing),
+    ("renormalise", _no_renorm, P.check_invariants),
+    ("renormalise", _no_renorm, P.check_brute_force),
+    ("swiglu_expert", _swapped_swiglu, P.check_single_expert_library),
+    ("swiglu_expert", _transposed_down,
+     lambda: P.check_brute_force(seed=11, T=16, d=12, E=5, k=2, n_shared=0, square=True)),
+    ("router_logits", _no_bias, P.check_brute_force),
+    ("silu", _sign_silu, P.check_silu),
+    ("expert_counts", _counts_off_by_one, P.check_worked_example_routing),
+    ("dispatch_order", _unstable_order, P.check_invariants),
+]
+
+
+@pytest.mark.parametrize("name,bad,check", MUTANTS,
+                         ids=[f"{m[0]}-{m[1].__name__}" for m in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, bad, check):
+    monkeypatch.setattr(om, name, bad)
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_dropped_shared_expert_is_caught(monkeypatch):
+    real = om.moe_forward
+
+    def no_shared(x, wr, b, k, efn, E, dtype, shared_fn=None, n_shared=0, tokens=None):
+        return real(x, wr, b, k, efn, E, dtype, None, 0, tokens)
+    monkeypatch.setattr(om, "moe_forward", no_shared)
+    with pytest.raises(AssertionError):
+        P.check_brute_force()
