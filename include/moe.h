@@ -1,0 +1,184 @@
+/*
+ * moe.h -- C ABI of a single-GPU (MI355X, gfx950) sparse top-k Mixture-of-Experts
+ * layer forward pass.
+ *
+ * The layer (page "Mixture of Experts Explained: Routers, Active Parameters and
+ * VRAM", the five numbered routing steps; page "Mixture of Experts (MoE):
+ * routing, expert parallelism, and memory", sections "How does MoE routing
+ * work" and "Shared experts"):
+ *
+ *   logits[t,e] = sum_c x[t,c] * w_router[e,c] + router_bias[e]
+ *   p[t,:]      = softmax(logits[t,:])                 over all E experts
+ *   idx[t,0..k) = the k largest logits, descending, exact ties -> lower e
+ *   w[t,j]      = p[t,idx[t,j]] / sum_j' p[t,idx[t,j']]   (renormalised)
+ *   FFN_e(v)    = (SiLU(v W_gate[e]^T) * (v W_up[e]^T)) W_down[e]^T   (SwiGLU)
+ *   y[t]        = sum_{j<k} w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])
+ *
+ * Tokens are grouped by expert before the expert multiplies (page "Mixture of
+ * experts: how MoE works and what it costs", section "What mixture of experts
+ * costs in compute"; page "Mixture of Experts: why a model with 671 billion
+ * parameters uses only 37", the router section's per-expert loop); every
+ * (token, slot) pair is computed, none is dropped.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *    and contiguous, 16-byte aligned.  The library never allocates or frees
+ *    memory; scratch comes from the caller's workspace.
+ *  - Storage types: `dtype` of the descriptor applies to x and every weight
+ *    (MOE_BF16: bfloat16 bit patterns; MOE_F32: IEEE float).  Router bias,
+ *    routing weights and expert outputs are float32.  MOE_BF16 computes with
+ *    bf16 products and float32 accumulation; MOE_F32 computes in float32.
+ *  - Arguments are validated on the host, synchronously, before any launch;
+ *    a failed check returns a negative moe_status and launches nothing.
+ *  - GPU work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream); outputs are valid once the stream has reached it.
+ *    A launch error returns MOE_ERR_HIP.
+ *  - T == 0 returns MOE_OK once the descriptor is valid, without reading any
+ *    pointer (workspace included) or launching anything.
+ *  - Calls that share a workspace must be ordered on one stream.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, pointer or enum is out of range        */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape this build rejects    */
+  MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than needed  */
+  MOE_ERR_HIP = -4          /* a HIP call or kernel launch failed             */
+} moe_status;
+
+/* Which expert-GEMM kernels run.  AUTO picks DECODE when the mean number of
+ * rows per routed expert, T*k/E, is at most 64, else PREFILL.  MOE_F32 layers
+ * always use their float32 kernels. */
+typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2 } moe_path;
+
+typedef struct moe_desc {
+  int64_t T;          /* tokens, >= 0                                        */
+  int32_t d;          /* hidden size                                         */
+  int32_t E;          /* routed experts, 1..512                              */
+  int32_t k;          /* experts per token, 1..min(E,32)                     */
+  int32_t ffn;        /* routed expert FFN width                             */
+  int32_t n_shared;   /* always-on shared experts, 0..8                      */
+  int32_t ffn_shared; /* their FFN width (ignored when n_shared == 0)        */
+  int32_t dtype;      /* moe_dtype of x and all weights                      */
+  int32_t y_dtype;    /* moe_dtype of y                                      */
+  int32_t path;       /* moe_path                                            */
+  int32_t flags;      /* reserved, must be 0                                 */
+} moe_desc;
+
+/* Stream handle: a hipStream_t passed as an opaque pointer. */
+typedef void* moe_stream;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text for a moe_status value. */
+const char* moe_status_str(int status);
+
+/* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG (T<0, d/E/k/
+ * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
+ * n_shared > 0, bad enum, flags != 0, T*(k+n_shared) >= 2^31) or
+ * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
+ * 64; MOE_F32 with any of them not a multiple of 4). */
+int moe_validate(const moe_desc* desc);
+
+/* Bytes of workspace every entry point below needs for `desc` (host only). */
+int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* The path AUTO resolves to for `desc` (host only; returns a moe_path, or a
+ * negative moe_status if the descriptor is invalid). */
+int moe_resolve_path(const moe_desc* desc);
+
+/* Rows of the grouped (permuted) layout: T*k routed rows followed by
+ * T*n_shared shared rows (host only; negative moe_status if invalid). */
+int64_t moe_grouped_rows(const moe_desc* desc);
+
+/*
+ * Whole layer forward (all steps below, in order, on one stream).
+ *   x            [T,d]            dtype
+ *   w_router     [E,d]            dtype
+ *   router_bias  [E]              float32, or NULL for none
+ *   w_up, w_gate [E,ffn,d]        dtype  (stacked per expert, K-contiguous)
+ *   w_down       [E,d,ffn]        dtype
+ *   ws_up, ws_gate [n_shared,ffn_shared,d], ws_down [n_shared,d,ffn_shared];
+ *                NULL when n_shared == 0 (required otherwise)
+ *   y            [T,d]            y_dtype (output)
+ *   topk_idx     [T,k] int32      optional output (NULL: kept in workspace)
+ *   topk_w       [T,k] float32    optional output
+ *   expert_counts [E] int32       optional output: (token, slot) pairs per expert
+ *   workspace    >= moe_workspace_size(desc) bytes, 256-byte aligned
+ */
+int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
+                const float* router_bias, const void* w_up, const void* w_gate,
+                const void* w_down, const void* ws_up, const void* ws_gate,
+                const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                moe_stream stream);
+
+/*
+ * Step 1-3: router logits, softmax, top-k and renormalisation (page "Mixture
+ * of Experts Explained...", steps Score, Normalise, Keep the top k,
+ * Renormalise).  Logits are accumulated in float32; selection compares float32
+ * logits, ties to the lower index.
+ *   topk_idx [T,k] int32 (required), topk_w [T,k] float32 (required).
+ */
+int moe_route(const moe_desc* desc, const void* x, const void* w_router,
+              const float* router_bias, int32_t* topk_idx, float* topk_w,
+              void* workspace, size_t workspace_bytes, moe_stream stream);
+
+/*
+ * Step 4: histogram, prefix scan and permutation that group the (token, slot)
+ * pairs by expert.  Outputs (all required):
+ *   expert_counts [E]        pairs routed to each expert
+ *   group_offsets [E+n_shared+1]  first grouped row of each group: routed
+ *                 experts 0..E-1 in order, then shared experts; the last entry
+ *                 is the row count T*(k+n_shared)
+ *   sorted_token  [T*(k+n_shared)] token of each grouped row; within a routed
+ *                 group rows follow increasing t*k+j (a stable grouping);
+ *                 shared group s holds tokens 0..T-1 in order
+ *   slot_row      [T,k]      grouped row of pair (t,j)
+ */
+int moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* expert_counts,
+                 int32_t* group_offsets, int32_t* sorted_token, int32_t* slot_row,
+                 void* workspace, size_t workspace_bytes, moe_stream stream);
+
+/*
+ * Steps 5-6: grouped expert FFNs over the grouped rows (SwiGLU up/gate, then
+ * down).  For grouped row r of group g with token t = sorted_token[r]:
+ *   expert_out[r,:] = FFN_g(x[t,:])       float32 [T*(k+n_shared), d]
+ * group_offsets / sorted_token as produced by moe_dispatch.
+ */
+int moe_experts(const moe_desc* desc, const void* x, const void* w_up, const void* w_gate,
+                const void* w_down, const void* ws_up, const void* ws_gate,
+                const void* ws_down, const int32_t* group_offsets,
+                const int32_t* sorted_token, float* expert_out, void* workspace,
+                size_t workspace_bytes, moe_stream stream);
+
+/*
+ * Step 7: weighted combine (page "Mixture of Experts Explained...", step Run
+ * and combine; page "Mixture of Experts (MoE)...", "Shared experts"):
+ *   y[t,:] = sum_{j<k} topk_w[t,j] * expert_out[slot_row[t,j],:]
+ *            + sum_s expert_out[group_offsets[E+s] + t, :]
+ * summed in that order, in float32, then stored as y_dtype.
+ */
+int moe_combine(const moe_desc* desc, const float* expert_out, const float* topk_w,
+                const int32_t* slot_row, const int32_t* group_offsets, void* y,
+                moe_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,198 @@
+"""Torch-facing wrappers with the names of the C entry points.
+
+Tensors provide device memory and the stream; each wrapper checks shapes and
+dtypes, allocates outputs and workspace with ``torch.empty`` and calls the
+library.  No arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MoeDesc, MoeError
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+_PATHS = {"auto": _lib.PATH_AUTO, "prefill": _lib.PATH_PREFILL, "decode": _lib.PATH_DECODE}
+
+
+def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
+              dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto") -> MoeDesc:
+    return MoeDesc(T=T, d=d, E=E, k=k, ffn=ffn, n_shared=n_shared,
+                   ffn_shared=ffn_shared if n_shared else 0, dtype=_DT[dtype],
+                   y_dtype=_DT[y_dtype], path=_PATHS[path], flags=0)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def moe_validate(desc: MoeDesc) -> int:
+    return _lib.lib().moe_validate(ctypes.byref(desc))
+
+
+def moe_workspace_size(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lib().moe_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "moe_workspace_size")
+    return n.value
+
+
+def moe_resolve_path(desc: MoeDesc) -> str:
+    p = _lib.lib().moe_resolve_path(ctypes.byref(desc))
+    if p < 0:
+        raise MoeError(p, "moe_resolve_path")
+    return {v: k for k, v in _PATHS.items()}[p]
+
+
+def moe_grouped_rows(desc: MoeDesc) -> int:
+    r = _lib.lib().moe_grouped_rows(ctypes.byref(desc))
+    if r < 0:
+        raise MoeError(int(r), "moe_grouped_rows")
+    return int(r)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace(desc: MoeDesc, device) -> torch.Tensor:
+    return torch.empty(moe_workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Weights:
+    """Stacked layer weights (device tensors in the layer's storage dtype)."""
+    w_router: torch.Tensor                 # [E, d]
+    w_up: torch.Tensor                     # [E, ffn, d]
+    w_gate: torch.Tensor                   # [E, ffn, d]
+    w_down: torch.Tensor                   # [E, d, ffn]
+    bias: Optional[torch.Tensor] = None    # [E] float32
+    ws_up: Optional[torch.Tensor] = None   # [S, ffn_s, d]
+    ws_gate: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None  # [S, d, ffn_s]
+
+    def desc(self, T: int, k: int, y_dtype=torch.float32, path: str = "auto") -> MoeDesc:
+        E, ffn, d = self.w_up.shape
+        ns = 0 if self.ws_up is None else self.ws_up.shape[0]
+        fs = 0 if self.ws_up is None else self.ws_up.shape[1]
+        return make_desc(T, d, E, k, ffn, ns, fs, self.w_up.dtype, y_dtype, path)
+
+
+def _check_weights(W: Weights, x: torch.Tensor):
+    E, ffn, d = W.w_up.shape
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name in ("w_router", "w_up", "w_gate", "w_down", "ws_up", "ws_gate", "ws_down"):
+        t = getattr(W, name)
+        if t is not None and t.dtype != dt:
+            raise ValueError(f"{name} has dtype {t.dtype}, x has {dt}")
+    if tuple(W.w_router.shape) != (E, d) or tuple(W.w_gate.shape) != (E, ffn, d) \
+            or tuple(W.w_down.shape) != (E, d, ffn) or x.shape[-1] != d:
+        raise ValueError("weight shapes do not match")
+    if W.bias is not None and (W.bias.dtype != torch.float32 or tuple(W.bias.shape) != (E,)):
+        raise ValueError("bias must be float32 [E]")
+
+
+def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path: str = "auto",
+                ws: Optional[torch.Tensor] = None, return_routing: bool = False):
+    """y = MoE(x).  With return_routing, also (topk_idx, topk_w, expert_counts)."""
+    _check_weights(W, x)
+    T = x.shape[0]
+    desc = W.desc(T, k, y_dtype, path)
+    dev = x.device
+    if ws is None:
+        ws = workspace(desc, dev)
+    y = torch.empty((T, x.shape[1]), dtype=y_dtype, device=dev)
+    idx = w = counts = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((W.w_up.shape[0],), dtype=torch.int32, device=dev)
+    st = _lib.lib().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(W.w_router), _ptr(W.bias),
+                                _ptr(W.w_up), _ptr(W.w_gate), _ptr(W.w_down), _ptr(W.ws_up),
+                                _ptr(W.ws_gate), _ptr(W.ws_down), _ptr(y), _ptr(idx), _ptr(w),
+                                _ptr(counts), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "moe_forward")
+    return (y, idx, w, counts) if return_routing else y
+
+
+def moe_route(x: torch.Tensor, W: Weights, k: int, ws: Optional[torch.Tensor] = None):
+    """(topk_idx [T,k] int32, topk_w [T,k] float32)."""
+    _check_weights(W, x)
+    T = x.shape[0]
+    desc = W.desc(T, k)
+    dev = x.device
+    ws = workspace(desc, dev) if ws is None else ws
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(_lib.lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(W.w_router), _ptr(W.bias),
+                                _ptr(idx), _ptr(w), _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_route")
+    return idx, w
+
+
+def moe_dispatch(desc: MoeDesc, topk_idx: torch.Tensor, ws: Optional[torch.Tensor] = None):
+    """(expert_counts [E], group_offsets [G+1], sorted_token [R], slot_row [T,k])."""
+    dev = topk_idx.device
+    if topk_idx.dtype != torch.int32 or tuple(topk_idx.shape) != (desc.T, desc.k):
+        raise ValueError("topk_idx must be int32 [T,k]")
+    ws = workspace(desc, dev) if ws is None else ws
+    R = moe_grouped_rows(desc)
+    counts = torch.empty((desc.E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((desc.E + desc.n_shared + 1,), dtype=torch.int32, device=dev)
+    sorted_token = torch.empty((R,), dtype=torch.int32, device=dev)
+    slot_row = torch.empty((desc.T, desc.k), dtype=torch.int32, device=dev)
+    _check(_lib.lib().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts),
+                                   _ptr(offsets), _ptr(sorted_token), _ptr(slot_row), _ptr(ws),
+                                   ws.numel(), _stream(dev)), "moe_dispatch")
+    return counts, offsets, sorted_token, slot_row
+
+
+def moe_experts(x: torch.Tensor, W: Weights, k: int, group_offsets: torch.Tensor,
+                sorted_token: torch.Tensor, path: str = "auto",
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """expert_out [R, d] float32: FFN of each grouped row's group."""
+    _check_weights(W, x)
+    desc = W.desc(x.shape[0], k, path=path)
+    dev = x.device
+    ws = workspace(desc, dev) if ws is None else ws
+    R = moe_grouped_rows(desc)
+    if group_offsets.dtype != torch.int32 or sorted_token.dtype != torch.int32 \
+            or group_offsets.numel() != desc.E + desc.n_shared + 1 or sorted_token.numel() != R:
+        raise ValueError("group_offsets / sorted_token do not match the layer")
+    out = torch.empty((R, x.shape[1]), dtype=torch.float32, device=dev)
+    _check(_lib.lib().moe_experts(ctypes.byref(desc), _ptr(x), _ptr(W.w_up), _ptr(W.w_gate),
+                                  _ptr(W.w_down), _ptr(W.ws_up), _ptr(W.ws_gate),
+                                  _ptr(W.ws_down), _ptr(group_offsets), _ptr(sorted_token),
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), "moe_experts")
+    return out
+
+
+def moe_combine(desc: MoeDesc, expert_out: torch.Tensor, topk_w: torch.Tensor,
+                slot_row: torch.Tensor, group_offsets: torch.Tensor,
+                y_dtype=torch.float32) -> torch.Tensor:
+    """y [T, d] from the expert outputs."""
+    dev = expert_out.device
+    if expert_out.dtype != torch.float32 or topk_w.dtype != torch.float32:
+        raise ValueError("expert_out and topk_w must be float32")
+    y = torch.empty((desc.T, desc.d), dtype=y_dtype, device=dev)
+    _check(_lib.lib().moe_combine(ctypes.byref(desc), _ptr(expert_out), _ptr(topk_w),
+                                  _ptr(slot_row), _ptr(group_offsets), _ptr(y), _stream(dev)),
+           "moe_combine")
+    return y

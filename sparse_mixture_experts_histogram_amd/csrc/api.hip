@@ -1,0 +1,151 @@
+// The extern "C" entry points of include/moe.h that launch work: host-side
+// checks, workspace carving and the launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+#include "plan.h"
+
+namespace moe {
+namespace {
+
+struct Ws {
+  char* base;
+  template <typename T>
+  T* at(size_t off) const {
+    return (T*)(base + off);
+  }
+};
+
+// MOE_OK with *empty set when the call has nothing to do (T == 0).
+int prepare(const moe_desc* d, void* workspace, size_t ws_bytes, Plan* P, bool* empty) {
+  int st = make_plan(d, P);
+  if (st != MOE_OK) return st;
+  *empty = d->T == 0;
+  if (*empty) return MOE_OK;
+  if (!workspace || ws_bytes < P->total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace) & 255) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+inline int hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)               \
+  do {                              \
+    int _st = hip_ok(expr);         \
+    if (_st != MOE_OK) return _st;  \
+  } while (0)
+
+bool shared_ok(const moe_desc* d, const void* a, const void* b, const void* c) {
+  return d->n_shared == 0 || (a && b && c);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
+                const void* w_up, const void* w_gate, const void* w_down, const void* ws_up,
+                const void* ws_gate, const void* ws_down, void* y, int32_t* topk_idx,
+                float* topk_w, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                moe_stream stream) {
+  Plan P;
+  bool empty = false;
+  int st = prepare(d, workspace, workspace_bytes, &P, &empty);
+  if (st != MOE_OK || empty) return st;
+  if (!x || !w_router || !w_up || !w_gate || !w_down || !y) return MOE_ERR_INVALID_ARG;
+  if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Ws W{(char*)workspace};
+  int32_t* idx = topk_idx ? topk_idx : W.at<int32_t>(P.o_idx);
+  float* w = topk_w ? topk_w : W.at<float>(P.o_w);
+  int32_t* counts = expert_counts ? expert_counts : W.at<int32_t>(P.o_counts);
+  int32_t* blk_hist = W.at<int32_t>(P.o_blk_hist);
+  int32_t* blk_rank = W.at<int32_t>(P.o_blk_rank);
+  int32_t* offsets = W.at<int32_t>(P.o_offsets);
+  int32_t* sorted = W.at<int32_t>(P.o_sorted);
+  int32_t* slot = W.at<int32_t>(P.o_slot);
+  Tile* tu = W.at<Tile>(P.o_tiles_up);
+  Tile* td = W.at<Tile>(P.o_tiles_down);
+  float* out = W.at<float>(P.o_out);
+  MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank, s));
+  MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
+  ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
+               W.at<void>(P.o_h), out};
+  MOE_TRY(launch_experts(P, a, s));
+  MOE_TRY(launch_combine(P, out, w, slot, offsets, y, s));
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
+              int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+              moe_stream stream) {
+  Plan P;
+  bool empty = false;
+  int st = prepare(d, workspace, workspace_bytes, &P, &empty);
+  if (st != MOE_OK || empty) return st;
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  Ws W{(char*)workspace};
+  MOE_TRY(launch_router(P, x, w_router, router_bias, topk_idx, topk_w,
+                        W.at<int32_t>(P.o_blk_hist), W.at<int32_t>(P.o_blk_rank),
+                        (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_dispatch(const moe_desc* d, const int32_t* topk_idx, int32_t* expert_counts,
+                 int32_t* group_offsets, int32_t* sorted_token, int32_t* slot_row,
+                 void* workspace, size_t workspace_bytes, moe_stream stream) {
+  Plan P;
+  bool empty = false;
+  int st = prepare(d, workspace, workspace_bytes, &P, &empty);
+  if (st != MOE_OK || empty) return st;
+  if (!topk_idx || !expert_counts || !group_offsets || !sorted_token || !slot_row)
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Ws W{(char*)workspace};
+  int32_t* blk_hist = W.at<int32_t>(P.o_blk_hist);
+  int32_t* blk_rank = W.at<int32_t>(P.o_blk_rank);
+  MOE_TRY(launch_block_hist(P, topk_idx, blk_hist, blk_rank, s));
+  MOE_TRY(launch_dispatch(P, topk_idx, blk_hist, blk_rank, expert_counts, group_offsets,
+                          sorted_token, slot_row, W.at<Tile>(P.o_tiles_up),
+                          W.at<Tile>(P.o_tiles_down), s));
+  return MOE_OK;
+}
+
+int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* w_gate,
+                const void* w_down, const void* ws_up, const void* ws_gate, const void* ws_down,
+                const int32_t* group_offsets, const int32_t* sorted_token, float* expert_out,
+                void* workspace, size_t workspace_bytes, moe_stream stream) {
+  Plan P;
+  bool empty = false;
+  int st = prepare(d, workspace, workspace_bytes, &P, &empty);
+  if (st != MOE_OK || empty) return st;
+  if (!x || !w_up || !w_gate || !w_down || !group_offsets || !sorted_token || !expert_out)
+    return MOE_ERR_INVALID_ARG;
+  if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Ws W{(char*)workspace};
+  Tile* tu = W.at<Tile>(P.o_tiles_up);
+  Tile* td = W.at<Tile>(P.o_tiles_down);
+  MOE_TRY(launch_tiles(P, group_offsets, tu, td, s));
+  ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted_token, tu, td,
+               W.at<void>(P.o_h), expert_out};
+  MOE_TRY(launch_experts(P, a, s));
+  return MOE_OK;
+}
+
+int moe_combine(const moe_desc* d, const float* expert_out, const float* topk_w,
+                const int32_t* slot_row, const int32_t* group_offsets, void* y,
+                moe_stream stream) {
+  Plan P;
+  int st = make_plan(d, &P);
+  if (st != MOE_OK || d->T == 0) return st;
+  if (!expert_out || !topk_w || !slot_row || !group_offsets || !y) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_combine(P, expert_out, topk_w, slot_row, group_offsets, y,
+                         (hipStream_t)stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Weighted combine: y[t] = sum_{j<k} w[t,j] * out[slot_row[t,j]] + sum_s
+// out[offsets[E+s] + t], summed in that order in float32 (step "Run and
+// combine" of page "Mixture of Experts Explained: Routers, Active Parameters
+// and VRAM"; shared experts added with weight one per page "Mixture of Experts
+// (MoE): routing, expert parallelism, and memory", section "Shared
+// experts").  A gather per token, no atomics, so the result is deterministic.
+// HBM-bound: it reads (k + n_shared) float32 rows and writes one row per
+// token; each workgroup handles one token with 16-byte accesses.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <bool Y_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const int32_t* __restrict__ offsets, int d,
+                                                      int k, int E, int n_sh, void* y) {
+  const int t = blockIdx.x;
+  __shared__ int rows[kMaxTopK + kMaxShared];
+  __shared__ float wts[kMaxTopK];
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = slot_row[(int64_t)t * k + threadIdx.x];
+    wts[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+  } else if (threadIdx.x < k + n_sh) {
+    rows[threadIdx.x] = offsets[E + threadIdx.x - k] + t;
+  }
+  __syncthreads();
+  const int d4 = d >> 2;
+  for (int c = threadIdx.x; c < d4; c += blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 v = ((const float4*)(out + (int64_t)rows[j] * d))[c];
+      const float wj = wts[j];
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    for (int s = 0; s < n_sh; ++s) {
+      const float4 v = ((const float4*)(out + (int64_t)rows[k + s] * d))[c];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    if (Y_BF16) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+      ((uint2*)((uint16_t*)y + (int64_t)t * d))[c] = pk;
+    } else {
+      ((float4*)((float*)y + (int64_t)t * d))[c] = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const Plan& P, const float* out, const float* w, const int32_t* slot_row,
+                          const int32_t* offsets, void* y, hipStream_t s) {
+  const moe_desc& D = P.desc;
+  const dim3 grid((unsigned)D.T), block(256);
+  if (D.y_dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, out, w, slot_row, offsets, D.d,
+                       D.k, D.E, D.n_shared, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, out, w, slot_row, offsets, D.d,
+                       D.k, D.E, D.n_shared, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Launch wrappers of the gfx950 kernels (host side).  Each returns the
+// hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace moe {
+
+// Router logits + softmax + top-k + renormalise; also writes the per-block
+// histogram and in-block stable ranks of the (token, slot) pairs.
+hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
+                         int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
+                         hipStream_t s);
+
+// Per-block histogram and ranks from given top-k indices.
+hipError_t launch_block_hist(const Plan& P, const int32_t* idx, int32_t* blk_hist,
+                             int32_t* blk_rank, hipStream_t s);
+
+// Scan + permute + tile schedules (one workgroup).  blk_hist is turned into
+// per-block exclusive offsets in place.
+hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,
+                           const int32_t* blk_rank, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up,
+                           Tile* tiles_down, hipStream_t s);
+
+// Tile schedules from given group offsets (one workgroup).
+hipError_t launch_tiles(const Plan& P, const int32_t* offsets, Tile* tiles_up, Tile* tiles_down,
+                        hipStream_t s);
+
+struct ExpertArgs {
+  const void* x;
+  const void *w_up, *w_gate, *w_down, *ws_up, *ws_gate, *ws_down;
+  const int32_t* sorted_token;
+  const Tile* tiles_up;
+  const Tile* tiles_down;
+  void* h;
+  float* out;
+};
+
+// Grouped up/gate GEMM + SwiGLU, then grouped down GEMM.
+hipError_t launch_experts(const Plan& P, const ExpertArgs& a, hipStream_t s);
+
+// y[t] = sum_j w[t,j] out[slot_row[t,j]] + sum_s out[offsets[E+s]+t].
+hipError_t launch_combine(const Plan& P, const float* out, const float* w, const int32_t* slot_row,
+                          const int32_t* offsets, void* y, hipStream_t s);
+
+}  // namespace moe

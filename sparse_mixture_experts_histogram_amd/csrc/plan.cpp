@@ -1,0 +1,151 @@
+// Host-side validation, path choice and workspace layout (no HIP calls).
+#include "plan.h"
+
+#include <algorithm>
+
+namespace moe {
+
+int row_tile(int kind) {
+  switch (kind) {
+    case KIND_F32: return 32;
+    default: return 128;
+  }
+}
+int up_col_tile(int kind) {
+  switch (kind) {
+    case KIND_F32: return 32;
+    default: return 64;
+  }
+}
+int down_col_tile(int kind) {
+  switch (kind) {
+    case KIND_F32: return 32;
+    default: return 128;
+  }
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int validate(const moe_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->d < 1 || d->E < 1 || d->k < 1 || d->ffn < 1) return MOE_ERR_INVALID_ARG;
+  if (d->E > kMaxExperts || d->k > kMaxTopK || d->k > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_ERR_INVALID_ARG;
+  if (d->n_shared > 0 && d->ffn_shared < 1) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->y_dtype != MOE_F32 && d->y_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_DECODE) return MOE_ERR_INVALID_ARG;
+  if (d->flags != 0) return MOE_ERR_INVALID_ARG;
+  const int64_t rows = d->T * (int64_t)(d->k + d->n_shared);
+  if (rows + kRowSlack >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARG;
+  const int q = d->dtype == MOE_BF16 ? 64 : 4;
+  if (d->d % q || d->ffn % q) return MOE_ERR_UNSUPPORTED;
+  if (d->n_shared > 0 && d->ffn_shared % q) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int make_plan(const moe_desc* d, Plan* p) {
+  int st = validate(d);
+  if (st != MOE_OK) return st;
+  Plan P{};
+  P.desc = *d;
+  const int64_t T = d->T;
+  P.G = d->E + d->n_shared;
+  P.pairs = T * d->k;
+  P.R = T * (int64_t)(d->k + d->n_shared);
+  P.nblk = cdiv(T, kRouterTokens);
+  P.ffn_max = d->n_shared > 0 ? std::max(d->ffn, d->ffn_shared) : d->ffn;
+  if (d->path == MOE_PATH_AUTO)
+    P.path = (T * d->k <= 64LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  else
+    P.path = d->path;
+  if (d->dtype == MOE_F32)
+    P.kind = KIND_F32;
+  else
+    P.kind = P.path == MOE_PATH_DECODE ? KIND_BF16_DECODE : KIND_BF16_PREFILL;
+
+  const int bm = row_tile(P.kind);
+  const int64_t nz = std::min<int64_t>(d->E, P.pairs);
+  P.max_row_tiles = (P.pairs + nz * (bm - 1)) / bm + d->n_shared * cdiv(T, bm);
+  auto shape = [&](int bn, int ncols, int ncols_sh) {
+    GemmShape s{};
+    s.bm = bm;
+    s.bn = bn;
+    s.n_cols = ncols;
+    s.n_cols_shared = d->n_shared > 0 ? ncols_sh : ncols;
+    s.n_tiles = (int)cdiv(std::max(s.n_cols, s.n_cols_shared), bn);
+    s.max_tiles = P.max_row_tiles * s.n_tiles;
+    return s;
+  };
+  P.up = shape(up_col_tile(P.kind), d->ffn, d->ffn_shared);
+  P.down = shape(down_col_tile(P.kind), d->d, d->d);
+
+  const size_t A = 256;
+  const size_t eb = d->dtype == MOE_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + std::max<size_t>(bytes, 1), A);
+    return at;
+  };
+  const size_t rows_ws = (size_t)P.R + kRowSlack;
+  P.o_blk_hist = take((size_t)P.nblk * d->E * 4);
+  P.o_blk_rank = take((size_t)P.pairs * 4);
+  P.o_counts = take((size_t)d->E * 4);
+  P.o_offsets = take((size_t)(P.G + 1) * 4);
+  P.o_tiles_up = take((size_t)(P.up.max_tiles + 1) * sizeof(Tile));
+  P.o_tiles_down = take((size_t)(P.down.max_tiles + 1) * sizeof(Tile));
+  P.o_sorted = take(rows_ws * 4);
+  P.o_slot = take((size_t)P.pairs * 4);
+  P.o_idx = take((size_t)P.pairs * 4);
+  P.o_w = take((size_t)P.pairs * 4);
+  P.o_h = take(rows_ws * (size_t)P.ffn_max * eb);
+  P.o_out = take(rows_ws * (size_t)d->d * 4);
+  P.total = o;
+  *p = P;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: argument out of range";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by this build";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_validate(const moe_desc* d) { return moe::validate(d); }
+
+int moe_workspace_size(const moe_desc* d, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe::Plan p;
+  int st = moe::make_plan(d, &p);
+  if (st != MOE_OK) return st;
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+int moe_resolve_path(const moe_desc* d) {
+  moe::Plan p;
+  int st = moe::make_plan(d, &p);
+  return st != MOE_OK ? st : p.path;
+}
+
+int64_t moe_grouped_rows(const moe_desc* d) {
+  moe::Plan p;
+  int st = moe::make_plan(d, &p);
+  return st != MOE_OK ? st : p.R;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Host-side plan of one layer call: validation, path choice, tile shapes and
+// the workspace layout.  Plain C++ (no HIP) so it can be built and checked on
+// a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Tokens per router workgroup (one block of the per-block histogram).
+constexpr int kRouterTokens = 16;
+// Largest supported expert count / top-k / shared experts.
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 8;
+// Rows of slack after the grouped rows so tile loads past the end stay in bounds.
+constexpr int kRowSlack = 256;
+
+// One GEMM tile: rows [m0, m_end) of group g, output columns [n0, n0 + BN).
+struct Tile {
+  int32_t g, m0, m_end, n0;
+};
+
+// Shape of one grouped-GEMM launch.
+struct GemmShape {
+  int bm;      // rows (tokens) per tile
+  int bn;      // output columns per tile
+  int n_cols;  // output columns of a routed group (ffn for up/gate, d for down)
+  int n_cols_shared;
+  int n_tiles;         // column tiles of the widest group
+  int64_t max_tiles;   // upper bound of (row tile, column tile) pairs
+};
+
+struct Plan {
+  moe_desc desc;
+  int path;          // resolved moe_path
+  int G;             // groups = E + n_shared
+  int64_t R;         // grouped rows = T*(k+n_shared)
+  int64_t pairs;     // T*k
+  int64_t nblk;      // router blocks
+  int ffn_max;       // max(ffn, ffn_shared)
+  int kind;          // kernel family, see KernelKind
+  GemmShape up, down;
+  int64_t max_row_tiles;
+  // workspace byte offsets
+  size_t o_blk_hist, o_blk_rank, o_counts, o_offsets, o_tiles_up, o_tiles_down, o_sorted,
+      o_slot, o_idx, o_w, o_h, o_out, total;
+};
+
+enum KernelKind { KIND_F32 = 0, KIND_BF16_PREFILL = 1, KIND_BF16_DECODE = 2 };
+
+// Fill `p` for `d`; returns a moe_status.
+int make_plan(const moe_desc* d, Plan* p);
+
+// Column-tile counts and tile-shape choices (shared with the kernels' launch code).
+int row_tile(int kind);
+int up_col_tile(int kind);
+int down_col_tile(int kind);
+
+}  // namespace moe

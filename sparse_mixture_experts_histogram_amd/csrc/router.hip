@@ -1,0 +1,258 @@
+// Router: logits (x times the E x d router matrix, plus an optional per-expert
+// bias), softmax, top-k with lowest-index ties, renormalisation of the kept
+// probabilities, and the per-block expert histogram of the chosen pairs.
+//
+// Steps "Score", "Normalise", "Keep the top k" and "Renormalise" of page
+// "Mixture of Experts Explained: Routers, Active Parameters and VRAM"; the
+// router as one bias-free linear layer per page "Mixture of Experts: why a
+// model with 671 billion parameters uses only 37", section "The router".
+//
+// One workgroup (4 waves) owns kRouterTokens tokens and every expert.  The
+// bf16 variant computes the logit tile with 16x16x32 bf16 MFMAs (exact bf16
+// products, fp32 accumulation); when E is small the K range is split across
+// waves and the partial tiles are summed in a fixed order.  Selection runs one
+// wave per token on 64-bit keys (order-preserving fp32 logit, then 2^32-1-e),
+// so a wave-wide max picks the largest logit and, among exact ties, the lowest
+// expert index.  Only the kept logits are needed for the weights:
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), which equals renormalising the
+// full softmax (page "Mixture of Experts Explained...", section "Softmax
+// before or after the top-k step").
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Histogram of one block's pairs and each pair's rank among earlier pairs of
+// the same expert (sel holds the block's n_pairs expert ids in pair order).
+__device__ void block_hist_rank(const int32_t* sel, int n_pairs, int E, int32_t* hist_out,
+                                int32_t* rank_out) {
+  for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
+    const int e = sel[p];
+    int r = 0;
+    for (int q = 0; q < p; ++q) r += (sel[q] == e);
+    rank_out[p] = r;
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int q = 0; q < n_pairs; ++q) c += (sel[q] == e);
+    hist_out[e] = c;
+  }
+}
+
+// Top-k of the tokens of one block from LDS logits lg[tl*ld + e].
+template <int EPL>
+__device__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int t0, int T,
+                           int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                           int32_t* sel) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int tl = wave; tl < kRouterTokens; tl += 4) {
+    const int t = t0 + tl;
+    if (t >= T) break;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        const float v = lg[tl * ld + e] + (bias ? bias[e] : 0.0f);
+        key[i] = ((uint64_t)order_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+      } else {
+        key[i] = 0;
+      }
+    }
+    float v0 = 0.f, wsum = 0.f, my_w = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) m = key[i] > m ? key[i] : m;
+      m = wave_max_u64(m);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (key[i] == m) key[i] = 0;
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+      const float v = order_key_inv((uint32_t)(m >> 32));
+      if (j == 0) v0 = v;
+      const float ex = expf(v - v0);
+      wsum += ex;
+      if (lane == j) {
+        my_w = ex;
+        my_e = e;
+      }
+    }
+    if (lane < k) {
+      idx_out[(int64_t)t * k + lane] = my_e;
+      w_out[(int64_t)t * k + lane] = my_w / wsum;
+      sel[tl * k + lane] = my_e;
+    }
+  }
+}
+
+template <int EPL>
+__device__ void router_tail(float* lg, int ld, int32_t* sel, const float* bias, int t0, int T,
+                            int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
+                            int32_t* blk_rank) {
+  topk_block<EPL>(lg, ld, bias, t0, T, E, k, idx_out, w_out, sel);
+  __syncthreads();
+  const int nt = min(kRouterTokens, T - t0);
+  block_hist_rank(sel, nt * k, E, blk_hist + (int64_t)blockIdx.x * E,
+                  blk_rank + (int64_t)t0 * k);
+}
+
+__device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const float* bias, int t0,
+                                     int T, int E, int k, int32_t* idx_out, float* w_out,
+                                     int32_t* blk_hist, int32_t* blk_rank) {
+  if (E <= 64)
+    router_tail<1>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  else if (E <= 128)
+    router_tail<2>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  else if (E <= 256)
+    router_tail<4>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  else
+    router_tail<8>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+}
+
+// Dynamic LDS: KS partial logit tiles [KS][16][ld] floats, then sel[16*k].
+template <int NT>
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k, int KS, int32_t* idx_out,
+    float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
+  extern __shared__ float lds[];
+  const int etiles = (E + 15) >> 4;
+  const int ld = etiles * 16 + 4;
+  float* lg = lds;
+  int32_t* sel = (int32_t*)(lds + KS * kRouterTokens * ld);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int ks = wave % KS, tg = wave / KS, tstep = 4 / KS;
+
+  int row = t0 + (lane & 15);
+  row = row < T ? row : T - 1;
+  const uint16_t* xp = x + (int64_t)row * d + (lane >> 4) * 8;
+  const uint16_t* wp[NT];
+  f32x4 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    int e = (tg + i * tstep) * 16 + (lane & 15);
+    e = e < E ? e : E - 1;
+    wp[i] = wr + (int64_t)e * d + (lane >> 4) * 8;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nk = d >> 5;
+  const int c0 = ks * nk / KS, c1 = (ks + 1) * nk / KS;
+#pragma unroll 4
+  for (int c = c0; c < c1; ++c) {
+    const u32x4 a = *(const u32x4*)(xp + c * 32);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (tg + i * tstep < etiles) {
+        const u32x4 b = *(const u32x4*)(wp[i] + c * 32);
+        acc[i] = mfma16(a, b, acc[i]);
+      }
+    }
+  }
+  // D[m = token][n = expert]: lane holds expert (lane & 15), tokens 4*(lane>>4)+r
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int tile = tg + i * tstep;
+    if (tile < etiles) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        lg[(ks * kRouterTokens + 4 * (lane >> 4) + r) * ld + tile * 16 + (lane & 15)] = acc[i][r];
+    }
+  }
+  __syncthreads();
+  if (KS > 1) {
+    for (int i = threadIdx.x; i < kRouterTokens * ld; i += blockDim.x) {
+      float s = lg[i];
+      for (int q = 1; q < KS; ++q) s += lg[q * kRouterTokens * ld + i];
+      lg[i] = s;
+    }
+    __syncthreads();
+  }
+  router_tail_dispatch(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+}
+
+__global__ __launch_bounds__(256) void router_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
+    int32_t* blk_rank) {
+  extern __shared__ float lds[];
+  const int ld = E + 1;
+  float* lg = lds;
+  int32_t* sel = (int32_t*)(lds + kRouterTokens * ld);
+  const int t0 = blockIdx.x * kRouterTokens;
+  for (int p = threadIdx.x; p < kRouterTokens * E; p += blockDim.x) {
+    const int tl = p / E, e = p % E;
+    const int t = t0 + tl;
+    float acc = 0.f;
+    if (t < T) {
+      const float4* xr = (const float4*)(x + (int64_t)t * d);
+      const float4* wrow = (const float4*)(wr + (int64_t)e * d);
+      for (int c = 0; c < (d >> 2); ++c) {
+        const float4 a = xr[c], b = wrow[c];
+        acc = fmaf(a.x, b.x, acc);
+        acc = fmaf(a.y, b.y, acc);
+        acc = fmaf(a.z, b.z, acc);
+        acc = fmaf(a.w, b.w, acc);
+      }
+    }
+    lg[tl * ld + e] = acc;
+  }
+  __syncthreads();
+  router_tail_dispatch(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+}
+
+__global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                         int E, int k, int32_t* blk_hist,
+                                                         int32_t* blk_rank) {
+  extern __shared__ int32_t sel_lds[];
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int n = min(kRouterTokens, T - t0) * k;
+  for (int p = threadIdx.x; p < n; p += blockDim.x) sel_lds[p] = idx[(int64_t)t0 * k + p];
+  __syncthreads();
+  block_hist_rank(sel_lds, n, E, blk_hist + (int64_t)blockIdx.x * E, blk_rank + (int64_t)t0 * k);
+}
+
+hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
+                         int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
+                         hipStream_t s) {
+  const moe_desc& D = P.desc;
+  const dim3 grid((unsigned)P.nblk), block(256);
+  const size_t sel_bytes = (size_t)kRouterTokens * D.k * 4;
+  if (D.dtype == MOE_F32) {
+    const size_t lds = (size_t)kRouterTokens * (D.E + 1) * 4 + sel_bytes;
+    hipLaunchKernelGGL(router_f32_kernel, grid, block, lds, s, (const float*)x,
+                       (const float*)w_router, bias, (int)D.T, D.d, D.E, D.k, idx, w, blk_hist,
+                       blk_rank);
+    return hipGetLastError();
+  }
+  const int etiles = (D.E + 15) / 16;
+  const int KS = etiles == 1 ? 4 : etiles == 2 ? 2 : 1;
+  const int nt = (etiles + (4 / KS) - 1) / (4 / KS);
+  const size_t lds = (size_t)KS * kRouterTokens * (etiles * 16 + 4) * 4 + sel_bytes;
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, lds, s, (const uint16_t*)x, (const uint16_t*)w_router,
+                       bias, (int)D.T, D.d, D.E, D.k, KS, idx, w, blk_hist, blk_rank);
+  };
+  if (nt <= 1)
+    args(router_bf16_kernel<1>);
+  else if (nt <= 2)
+    args(router_bf16_kernel<2>);
+  else if (nt <= 4)
+    args(router_bf16_kernel<4>);
+  else
+    args(router_bf16_kernel<8>);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_hist(const Plan& P, const int32_t* idx, int32_t* blk_hist,
+                             int32_t* blk_rank, hipStream_t s) {
+  const moe_desc& D = P.desc;
+  hipLaunchKernelGGL(block_hist_kernel, dim3((unsigned)P.nblk), dim3(256),
+                     (size_t)kRouterTokens * D.k * 4, s, idx, (int)D.T, D.E, D.k, blk_hist,
+                     blk_rank);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+"""Helpers for the GPU parity tests: upload seeded cases and compare with the
+oracle.  Tolerances:
+
+* routing indices and per-expert counts: exact;
+* routing weights: |w - w_oracle| <= 1e-5 (float32 softmax over float32
+  logits that differ from the fp64 ones by ~1e-6);
+* y (and expert outputs): max |err| <= 2e-2 * rms(y_oracle) for bf16 layers,
+  <= 1e-4 * rms(y_oracle) for float32 layers.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import sparse_mixture_experts_histogram_amd as moe
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+W_TOL = 1e-5
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def upload(case):
+    c = case.cfg
+    W = moe.Weights(
+        w_router=to_dev(case.w_router, c.dtype),
+        w_up=to_dev(case.up, c.dtype), w_gate=to_dev(case.gate, c.dtype),
+        w_down=to_dev(case.down, c.dtype),
+        bias=None if case.bias is None else torch.from_numpy(case.bias).to("cuda"))
+    if c.n_shared:
+        W.ws_up = to_dev(case.s_up, c.dtype)
+        W.ws_gate = to_dev(case.s_gate, c.dtype)
+        W.ws_down = to_dev(case.s_down, c.dtype)
+    return to_dev(case.x, c.dtype), W
+
+
+def rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    return float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref))) / max(rms, 1e-300)
+
+
+def check_routing(idx_gpu, w_gpu, counts_gpu, ref):
+    idx = idx_gpu.cpu().numpy()
+    assert np.array_equal(idx, ref.idx), np.argwhere(idx != ref.idx)[:5]
+    if counts_gpu is not None:
+        assert np.array_equal(counts_gpu.cpu().numpy(), ref.counts)
+    werr = float(np.max(np.abs(w_gpu.cpu().numpy().astype(np.float64) - ref.w))) if idx.size else 0.0
+    assert werr <= W_TOL, werr
+    return werr
+
+
+def sample_tokens(T: int, n: int = 24, seed: int = 0) -> np.ndarray:
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(8, T - 8), size=n - 16, replace=False)
+    return np.unique(np.concatenate([np.arange(8), mid, np.arange(T - 8, T)]))

@@ -1,0 +1,101 @@
+"""The C ABI library: it loads, exports what include/moe.h declares, and its
+host-side checks return the documented status codes (no GPU work)."""
+import ctypes
+
+import pytest
+
+import sparse_mixture_experts_histogram_amd as moe
+from sparse_mixture_experts_histogram_amd import _lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def desc(**kw):
+    base = dict(T=64, d=256, E=8, k=2, ffn=512, n_shared=0, ffn_shared=0, dtype=1, y_dtype=0,
+                path=0, flags=0)
+    base.update(kw)
+    return _lib.MoeDesc(**base)
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = _lib.header_symbols()
+    assert {"moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_combine",
+            "moe_workspace_size", "moe_validate"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+def test_desc_struct_size():
+    assert ctypes.sizeof(_lib.MoeDesc) == 48
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK),
+    (dict(T=0), OK),
+    (dict(T=-1), INVALID),
+    (dict(k=0), INVALID),
+    (dict(k=9), INVALID),
+    (dict(E=0), INVALID),
+    (dict(E=513, k=2), INVALID),
+    (dict(E=64, k=33), INVALID),
+    (dict(n_shared=9, ffn_shared=64), INVALID),
+    (dict(n_shared=1, ffn_shared=0), INVALID),
+    (dict(dtype=2), INVALID),
+    (dict(y_dtype=5), INVALID),
+    (dict(path=3), INVALID),
+    (dict(flags=1), INVALID),
+    (dict(T=2 ** 30, k=2), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(ffn=100), UNSUPPORTED),
+    (dict(n_shared=1, ffn_shared=96), UNSUPPORTED),
+    (dict(dtype=0, d=36, ffn=20), OK),
+    (dict(dtype=0, d=34), UNSUPPORTED),
+    (dict(E=512, k=32, d=64, ffn=64), OK),
+])
+def test_validate_codes(kw, code):
+    assert moe.moe_validate(desc(**kw)) == code
+
+
+def test_workspace_and_paths():
+    d = desc(T=4096, d=4096, E=8, k=2, ffn=14336)
+    ws = moe.moe_workspace_size(d)
+    assert ws % 256 == 0
+    # grouped rows, h and fp32 expert outputs dominate
+    R = 4096 * 2
+    assert ws > (R * 14336 * 2 + R * 4096 * 4)
+    assert moe.moe_resolve_path(d) == "prefill"
+    assert moe.moe_resolve_path(desc(T=16, d=4096, E=8, k=2, ffn=14336)) == "decode"
+    assert moe.moe_resolve_path(desc(T=512, d=2880, E=128, k=4, ffn=2880)) == "decode"
+    assert moe.moe_resolve_path(desc(T=4096, d=7168, E=256, k=8, ffn=2048, n_shared=1,
+                                     ffn_shared=2048)) == "prefill"
+    assert moe.moe_grouped_rows(desc(T=10, k=3, n_shared=2, ffn_shared=64)) == 50
+
+
+def test_entry_points_reject_before_launch():
+    L = _lib.lib()
+    d = desc()
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(d), None) == INVALID
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    # missing workspace
+    assert L.moe_forward(ctypes.byref(d), *([None] * 13), None, 0, None) == WORKSPACE
+    # fake (never dereferenced) aligned workspace, missing tensors
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.moe_forward(ctypes.byref(d), *([None] * 13), fake, n.value, None) == INVALID
+    assert L.moe_forward(ctypes.byref(d), *([None] * 13), fake, n.value - 1, None) == WORKSPACE
+    misaligned = ctypes.c_void_p((1 << 20) + 16)
+    assert L.moe_route(ctypes.byref(d), None, None, None, None, None, misaligned, n.value,
+                       None) == WORKSPACE
+    bad = desc(k=0)
+    assert L.moe_combine(ctypes.byref(bad), None, None, None, None, None, None) == INVALID
+    assert L.moe_status_str(-3).startswith(b"MOE_ERR_WORKSPACE")
+
+
+def test_zero_tokens_touch_nothing():
+    L = _lib.lib()
+    d = desc(T=0)
+    assert L.moe_forward(ctypes.byref(d), *([None] * 13), None, 0, None) == OK
+    assert L.moe_route(ctypes.byref(d), None, None, None, None, None, None, 0, None) == OK
+    assert L.moe_combine(ctypes.byref(d), None, None, None, None, None, None) == OK
