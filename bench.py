@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the Mixtral-shaped layer (d=4096, E=8, top-2, SwiGLU ffn=14336, bf16
+storage, fp32 accumulation) at T=4096 tokens (prefill).  One step is one
+moe_forward over the whole batch (router, dispatch, both grouped GEMMs,
+combine), inputs and weights already resident in HBM.  The same layer at T=16
+(decode) is timed too and reported under "decode".
+
+Prints ONE JSON line with the metric, the live roofline figure of the
+dominant kernel (the up/gate grouped GEMM, timed with hipEvents recorded on
+its launch stream inside the timed steps) and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec; grouped-GEMM % MFMA peak (prefill), % HBM peak (decode)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the T=16 decode leg")
+    ap.add_argument("--cpu-sample", type=int, default=1024,
+                    help="tokens of the workload the CPU oracle runs")
+    return ap.parse_args()
+
+
+def upload_layer(cfg, T):
+    import numpy as np
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from moe_inputs import generate, tables
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(a).to("cuda")
+
+    li = tables.layer_inputs(cfg, T)
+    E = cfg.E
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    up = torch.empty((E, cfg.ffn, cfg.d), dtype=dt, device="cuda")
+    gate = torch.empty_like(up)
+    down = torch.empty((E, cfg.d, cfg.ffn), dtype=dt, device="cuda")
+    for e, (u, g, dn) in generate.iter_experts(cfg, range(E)):
+        up[e].copy_(dev(u))
+        gate[e].copy_(dev(g))
+        down[e].copy_(dev(dn))
+    W = moe.Weights(w_router=dev(li.w_router), w_up=up, w_gate=gate, w_down=down,
+                    bias=None if li.bias is None else torch.from_numpy(li.bias).cuda())
+    return li, dev(li.x), W
+
+
+def time_forward(x, W, k, steps, warmup):
+    """K timed steps bracketed by synchronize; per-kernel durations from the
+    events each step records on its own launch stream."""
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from sparse_mixture_experts_histogram_amd.hipevents import Events
+
+    T = x.shape[0]
+    desc = W.desc(T, k)
+    ws = moe.workspace(desc, x.device)
+    y = torch.empty((T, x.shape[1]), dtype=torch.float32, device=x.device)
+    counts = torch.empty((W.w_up.shape[0],), dtype=torch.int32, device=x.device)
+    ev = Events(6 * max(steps, 1))
+    for _ in range(warmup):
+        moe.moe_forward_timed(x, W, k, None, y, ws, counts=counts)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    names = ["router", "dispatch", "expert_up", "expert_down", "combine"]
+    per = {n: statistics.mean(ev.ms(6 * i + j, 6 * i + j + 1) for i in range(steps))
+           for j, n in enumerate(names)}
+    layer = statistics.mean(ev.ms(6 * i, 6 * i + 5) for i in range(steps))
+    ev.close()
+    return wall, layer, per, counts.cpu().numpy()
+
+
+def time_decode(x, W, k, iters):
+    """Per-iteration event timing with the 256 MB MALL flushed (a 1 GiB write)
+    between iterations, outside the timed interval; median."""
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from sparse_mixture_experts_histogram_amd.hipevents import Events
+
+    T = x.shape[0]
+    ws = moe.workspace(W.desc(T, k), x.device)
+    y = torch.empty((T, x.shape[1]), dtype=torch.float32, device=x.device)
+    counts = torch.empty((W.w_up.shape[0],), dtype=torch.int32, device=x.device)
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=x.device)
+    ev = Events(6 * iters)
+    for _ in range(5):
+        moe.moe_forward_timed(x, W, k, None, y, ws, counts=counts)
+    for i in range(iters):
+        flush.zero_()
+        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+    torch.cuda.synchronize()
+    layer = statistics.median(ev.ms(6 * i, 6 * i + 5) for i in range(iters))
+    gemm = statistics.median(ev.ms(6 * i + 2, 6 * i + 4) for i in range(iters))
+    ev.close()
+    del flush
+    return layer, gemm, counts.cpu().numpy()
+
+
+def decode_leg(cfg, x, W, k, iters):
+    import numpy as np
+    xd = x[:16].contiguous()
+    dec_layer, dec_gemm, dec_counts = time_decode(xd, W, k, iters)
+    touched = int(np.sum(dec_counts > 0))
+    touched_bytes = touched * 3 * cfg.d * cfg.ffn * 2
+    dec = {"T": 16, "ms_per_step": round(dec_layer, 4), "tokens_per_s": round(16 / dec_layer * 1e3, 1),
+           "experts_touched": touched, "touched_weight_bytes": touched_bytes,
+           "hbm_frac_layer": round(touched_bytes / (dec_layer * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+           "hbm_frac_expert_gemms": round(touched_bytes / (dec_gemm * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+           "timing": "median of per-iteration hipEvent times, MALL flushed between iterations"}
+
+    return dec
+
+
+def cpu_baseline(cfg, li, sample):
+    """The fp64 oracle as written, on the first `sample` tokens of the same
+    workload (routing and every chosen expert for those tokens)."""
+    import oracle
+    from moe_inputs import generate
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    xs = li.x[:sample]
+    # draw the weights outside the timed region (they are inputs, resident)
+    wts = {e: generate.expert_weights(cfg, e) for e in range(cfg.E)}
+    t0 = time.perf_counter()
+    oracle.moe_forward(xs, li.w_router, li.bias, cfg.k, lambda e: wts[e], cfg.E, cfg.dtype)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {sample} tokens of the {cfg.name} T={cfg.T} workload, fp64 numpy "
+                      f"oracle (routing + chosen experts), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert parallelism is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from moe_inputs import NAMED
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = NAMED["mixtral"]
+    T, k = 4096, cfg.k
+    t_in = time.perf_counter()
+    li, x, W = upload_layer(cfg, T)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_in:.1f}s", file=sys.stderr,
+          flush=True)
+
+    wall, layer, per, counts = time_forward(x, W, k, args.steps, args.warmup)
+    print(f"[bench] prefill: {wall * 1e3:.3f} ms/step wall, per-kernel ms {per}",
+          file=sys.stderr, flush=True)
+    flops_up = 4.0 * cfg.d * cfg.ffn * T * k
+    flops_down = 2.0 * cfg.d * cfg.ffn * T * k
+    flops_layer = cfg.flops(T)
+    up_tf = flops_up / (per["expert_up"] * 1e-3) / 1e12
+    gemm_tf = (flops_up + flops_down) / ((per["expert_up"] + per["expert_down"]) * 1e-3) / 1e12
+
+    # decode leg: same layer, first 16 tokens
+    dec = None
+    if not args.no_decode:
+        dec = decode_leg(cfg, x, W, k, args.decode_iters)
+        print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, li, args.cpu_sample)
+        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC, "value": round(T / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": "mixtral_prefill", "T": T, "d": cfg.d, "E": cfg.E, "k": k,
+                   "ffn": cfg.ffn, "n_shared": 0, "storage": "bf16", "accumulate": "fp32",
+                   "y": "fp32", "path": "prefill", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "expert_up (grouped up/gate GEMM + SwiGLU)",
+                     "achieved": round(up_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(up_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(per["expert_up"], 4),
+                     "algorithmic_flops_per_launch": flops_up},
+        "grouped_gemm_frac_mfma": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+        "layer_tflops": round(flops_layer / (layer * 1e-3) / 1e12, 2),
+        "kernels_ms": {kname: round(v, 4) for kname, v in per.items()},
+        "expert_counts": [int(c) for c in counts],
+        "decode": dec,
+        "cpu_baseline": cpu,
+        "host": {"cpu": platform.processor() or platform.machine(),
+                 "cores_visible": len(os.sched_getaffinity(0))},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -129,6 +129,20 @@ int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 moe_stream stream);
 
 /*
+ * moe_forward with timing marks: the same launches on the same stream, with
+ * events[i] (a hipEvent_t, or NULL to skip) recorded on `stream` before the
+ * router (0), dispatch (1), up/gate GEMM (2), down GEMM (3) and combine (4)
+ * kernels, and events[5] after the combine.  `events` points to 6 entries.
+ * For measuring each step's duration on the launch stream.
+ */
+int moe_forward_timed(const moe_desc* desc, const void* x, const void* w_router,
+                      const float* router_bias, const void* w_up, const void* w_gate,
+                      const void* w_down, const void* ws_up, const void* ws_gate,
+                      const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                      int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                      moe_stream stream, void* const* events);
+
+/*
  * Step 1-3: router logits, softmax, top-k and renormalisation (page "Mixture
  * of Experts Explained...", steps Score, Normalise, Keep the top k,
  * Renormalise).  Logits are accumulated in float32; selection compares float32

@@ -71,6 +71,8 @@ def lib():
     V = c_void_p
     L.moe_forward.restype = c_int
     L.moe_forward.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V]
+    L.moe_forward_timed.restype = c_int
+    L.moe_forward_timed.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V, V]
     L.moe_route.restype = c_int
     L.moe_route.argtypes = [D, V, V, V, V, V, V, c_size_t, V]
     L.moe_dispatch.restype = c_int

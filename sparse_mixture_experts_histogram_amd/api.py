@@ -132,6 +132,21 @@ def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path
     return (y, idx, w, counts) if return_routing else y
 
 
+def moe_forward_timed(x: torch.Tensor, W: Weights, k: int, events, y: torch.Tensor,
+                      ws: torch.Tensor, y_dtype=torch.float32, path: str = "auto",
+                      counts: Optional[torch.Tensor] = None) -> None:
+    """moe_forward into preallocated y/ws, recording the 6 hipEvents at
+    ``events`` (a void** from hipevents.Events.slice) around its launches."""
+    T = x.shape[0]
+    desc = W.desc(T, k, y_dtype, path)
+    st = _lib.lib().moe_forward_timed(ctypes.byref(desc), _ptr(x), _ptr(W.w_router),
+                                      _ptr(W.bias), _ptr(W.w_up), _ptr(W.w_gate),
+                                      _ptr(W.w_down), _ptr(W.ws_up), _ptr(W.ws_gate),
+                                      _ptr(W.ws_down), _ptr(y), None, None, _ptr(counts),
+                                      _ptr(ws), ws.numel(), _stream(x.device), events)
+    _check(st, "moe_forward_timed")
+
+
 def moe_route(x: torch.Tensor, W: Weights, k: int, ws: Optional[torch.Tensor] = None):
     """(topk_idx [T,k] int32, topk_w [T,k] float32)."""
     _check_weights(W, x)

@@ -42,15 +42,18 @@ bool shared_ok(const moe_desc* d, const void* a, const void* b, const void* c) {
 }  // namespace
 }  // namespace moe
 
-using namespace moe;
+namespace moe {
+namespace {
 
-extern "C" {
-
-int moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
-                const void* w_up, const void* w_gate, const void* w_down, const void* ws_up,
-                const void* ws_gate, const void* ws_down, void* y, int32_t* topk_idx,
-                float* topk_w, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
-                moe_stream stream) {
+// moe_forward's launch sequence; events[i] (when non-null) is recorded on the
+// stream before launch i (router, dispatch, up/gate, down, combine) and
+// events[5] after the last one.
+int forward_impl(const moe_desc* d, const void* x, const void* w_router,
+                 const float* router_bias, const void* w_up, const void* w_gate,
+                 const void* w_down, const void* ws_up, const void* ws_gate, const void* ws_down,
+                 void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                 void* workspace, size_t workspace_bytes, moe_stream stream,
+                 void* const* events) {
   Plan P;
   bool empty = false;
   int st = prepare(d, workspace, workspace_bytes, &P, &empty);
@@ -58,6 +61,10 @@ int moe_forward(const moe_desc* d, const void* x, const void* w_router, const fl
   if (!x || !w_router || !w_up || !w_gate || !w_down || !y) return MOE_ERR_INVALID_ARG;
   if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], s);
+    return hipSuccess;
+  };
   Ws W{(char*)workspace};
   int32_t* idx = topk_idx ? topk_idx : W.at<int32_t>(P.o_idx);
   float* w = topk_w ? topk_w : W.at<float>(P.o_w);
@@ -70,13 +77,48 @@ int moe_forward(const moe_desc* d, const void* x, const void* w_router, const fl
   Tile* tu = W.at<Tile>(P.o_tiles_up);
   Tile* td = W.at<Tile>(P.o_tiles_down);
   float* out = W.at<float>(P.o_out);
-  MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank, s));
-  MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
                W.at<void>(P.o_h), out};
-  MOE_TRY(launch_experts(P, a, s));
+  MOE_TRY(mark(0));
+  MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank, s));
+  MOE_TRY(mark(1));
+  MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
+  MOE_TRY(mark(2));
+  MOE_TRY(launch_expert_up(P, a, s));
+  MOE_TRY(mark(3));
+  MOE_TRY(launch_expert_down(P, a, s));
+  MOE_TRY(mark(4));
   MOE_TRY(launch_combine(P, out, w, slot, offsets, y, s));
+  MOE_TRY(mark(5));
   return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
+                const void* w_up, const void* w_gate, const void* w_down, const void* ws_up,
+                const void* ws_gate, const void* ws_down, void* y, int32_t* topk_idx,
+                float* topk_w, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                moe_stream stream) {
+  return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
+                      ws_down, y, topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+int moe_forward_timed(const moe_desc* d, const void* x, const void* w_router,
+                      const float* router_bias, const void* w_up, const void* w_gate,
+                      const void* w_down, const void* ws_up, const void* ws_gate,
+                      const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                      int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                      moe_stream stream, void* const* events) {
+  return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
+                      ws_down, y, topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
+                      stream, events);
 }
 
 int moe_route(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
@@ -132,7 +174,8 @@ int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* 
   MOE_TRY(launch_tiles(P, group_offsets, tu, td, s));
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted_token, tu, td,
                W.at<void>(P.o_h), expert_out};
-  MOE_TRY(launch_experts(P, a, s));
+  MOE_TRY(launch_expert_up(P, a, s));
+  MOE_TRY(launch_expert_down(P, a, s));
   return MOE_OK;
 }
 

@@ -286,35 +286,53 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 a) {
 }
 
 // ---------------------------------------------------------------- launch
-hipError_t launch_experts(const Plan& P, const ExpertArgs& x, hipStream_t s) {
+static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
   const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
+  return GemmArgs{(const uint16_t*)x.x, x.sorted_token, D.d, (const uint16_t*)x.w_up,
+                  (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
+                  (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
+                  x.tiles_up};
+}
+static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
+  const moe_desc& D = P.desc;
+  const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
+  return GemmArgs{(const uint16_t*)x.h, nullptr, P.ffn_max, (const uint16_t*)x.w_down, nullptr,
+                  (const uint16_t*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
+                  x.tiles_down};
+}
+
+hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
+  const moe_desc& D = P.desc;
   const dim3 block(256);
-  const dim3 grid_up((unsigned)(((P.up.max_tiles + 7) / 8) * 8));
-  const dim3 grid_dn((unsigned)(((P.down.max_tiles + 7) / 8) * 8));
+  const dim3 grid((unsigned)(((P.up.max_tiles + 7) / 8) * 8));
   if (P.kind == KIND_F32) {
+    const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
     GemmArgsF32 u{(const float*)x.x, x.sorted_token, D.d, (const float*)x.w_up,
                   (const float*)x.w_gate, (const float*)x.ws_up, (const float*)x.ws_gate,
                   D.E, D.ffn, ffn_s, D.d, D.d, (float*)x.h, P.ffn_max, x.tiles_up};
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, grid_up, block, 0, s, u);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, block, 0, s, u);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 64, 32, true>), grid, block, 0, s,
+                     up_args(P, x));
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s) {
+  const moe_desc& D = P.desc;
+  const dim3 block(256);
+  const dim3 grid((unsigned)(((P.down.max_tiles + 7) / 8) * 8));
+  if (P.kind == KIND_F32) {
+    const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
     GemmArgsF32 dn{(const float*)x.h, nullptr, P.ffn_max, (const float*)x.w_down, nullptr,
                    (const float*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
                    x.tiles_down};
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, grid_dn, block, 0, s, dn);
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, block, 0, s, dn);
     return hipGetLastError();
   }
-  GemmArgs u{(const uint16_t*)x.x, x.sorted_token, D.d, (const uint16_t*)x.w_up,
-             (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up, (const uint16_t*)x.ws_gate,
-             D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max, x.tiles_up};
-  GemmArgs dn{(const uint16_t*)x.h, nullptr, P.ffn_max, (const uint16_t*)x.w_down, nullptr,
-              (const uint16_t*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
-              x.tiles_down};
-  hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 64, 32, true>), grid_up, block, 0, s, u);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 64, false>), grid_dn, block, 0, s, dn);
+  hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 64, false>), grid, block, 0, s,
+                     down_args(P, x));
   return hipGetLastError();
 }
 

@@ -39,8 +39,10 @@ struct ExpertArgs {
   float* out;
 };
 
-// Grouped up/gate GEMM + SwiGLU, then grouped down GEMM.
-hipError_t launch_experts(const Plan& P, const ExpertArgs& a, hipStream_t s);
+// Grouped up/gate GEMM + SwiGLU (writes h).
+hipError_t launch_expert_up(const Plan& P, const ExpertArgs& a, hipStream_t s);
+// Grouped down GEMM (reads h, writes out).
+hipError_t launch_expert_down(const Plan& P, const ExpertArgs& a, hipStream_t s);
 
 // y[t] = sum_j w[t,j] out[slot_row[t,j]] + sum_s out[offsets[E+s]+t].
 hipError_t launch_combine(const Plan& P, const float* out, const float* w, const int32_t* slot_row,
