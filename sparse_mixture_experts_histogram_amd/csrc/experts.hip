@@ -14,8 +14,9 @@
 // token tile, so each lane ends with 4 consecutive output features of one
 // token, which it stores as one 8-byte (bf16 h) or 16-byte (fp32 out) write.
 // Both operands are K-contiguous in memory and staged through LDS in 64-wide
-// K slabs, double-buffered, with the 16-byte chunks of a row XOR-swizzled by
-// (row/2)%8 so that the 16 lanes of each ds_read_b128 phase hit distinct banks.
+// K slabs, double-buffered, with the 16-byte chunks of a row XOR-swizzled so
+// that the lanes of each ds_read_b128 phase hit distinct banks.  Fragments of
+// the next k-step are read from LDS while the current MFMAs run.
 // The up/gate tile holds the up and the gate rows of the same features, so
 // SwiGLU is applied in registers before h is written.
 //
@@ -42,10 +43,19 @@ struct GemmArgs {
   const Tile* tiles;
 };
 
-constexpr int BK = 64;  // K slab (8 chunks of 8 bf16 per row)
+constexpr int BK = 32;  // K slab: 4 chunks of 8 bf16 per tile row (64 bytes)
 
+// LDS element offset of 16-byte chunk `chunk` of tile row `row`.  A
+// ds_read_b128 phase serves 16 lanes that read one chunk of 16 consecutive
+// rows; XOR-ing the chunk with (row / 4) % 4 spreads them over all 64 banks.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+// A tile entry read by every lane, made wave-uniform (scalar registers).
+__device__ __forceinline__ Tile uniform_tile(const Tile& t) {
+  return Tile{__builtin_amdgcn_readfirstlane(t.g), __builtin_amdgcn_readfirstlane(t.m0),
+              __builtin_amdgcn_readfirstlane(t.m_end), __builtin_amdgcn_readfirstlane(t.n0)};
 }
 
 // Remap the workgroup index so consecutive tile-list entries share an XCD.
@@ -58,6 +68,27 @@ __device__ __forceinline__ int tile_of_block(const Tile* tiles) {
   return L < count ? L : -1;
 }
 
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediate that waits for at most `n` outstanding vector-memory
+// operations and nothing else (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkm0 = ~(15 << 8);  // AND into an immediate to also wait lgkmcnt(0)
+
+// One stage of a tile operand: 1 KB blocks of 16 rows, block b = wave + 4 i.
+// global_load_lds_dwordx4 fills bytes [16 l, 16 l + 16) of a block from lane
+// l, so lane l fetches row 16 b + l / 4 at the chunk whose swizzled slot is
+// l % 4.
+template <int NBLK>
+__device__ __forceinline__ void dma_tile(const char* base, const uint32_t* off, uint16_t* lds,
+                                         int wave) {
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
+                                     LDS_PTR(lds + (wave + 4 * i) * 512), 16, 0, 0);
+}
+
 template <int BM, int BN, int WM, int WN, bool UPGATE>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WROWS = UPGATE ? 2 * BN : BN;        // weight rows in the tile
@@ -65,13 +96,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(NWN * NWM == 4, "4 waves");
   constexpr int TN = WN / 32, TM = WM / 32;           // 32x32 sub-tiles per wave
   constexpr int NS = UPGATE ? 2 : 1;                  // up and gate, or down
-  constexpr int WCH = WROWS * 8 / 256;                // 16-byte chunks per thread
-  constexpr int XCH = BM * 8 / 256;
-  static_assert(WCH >= 1 && XCH >= 1, "tile too small");
+  constexpr int WB = WROWS / 64;                      // 1 KB blocks per wave and stage
+  constexpr int XB = BM / 64;
+  constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
+  static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
 
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
-  const Tile tl = a.tiles[1 + L];
+  const Tile tl = uniform_tile(a.tiles[1 + L]);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
   const int K = sh ? a.K_s : a.K_r;
@@ -81,43 +113,49 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const uint16_t* W1 = UPGATE ? (sh ? a.s1 + (tl.g - a.E) * wstride : a.w1 + tl.g * wstride)
                               : nullptr;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lw[2][WROWS * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lx[2][BM * BK];
+  // Four stage buffers per operand, as separate arrays so the compiler can
+  // tell reads of one buffer from DMA still landing in another.
+  __shared__ __attribute__((aligned(1024))) uint16_t lw0[WROWS * BK], lw1[WROWS * BK],
+      lw2[WROWS * BK], lw3[WROWS * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t lx0[BM * BK], lx1[BM * BK], lx2[BM * BK],
+      lx3[BM * BK];
 
   const int tid = threadIdx.x;
-  // global source of each of this thread's chunks (row pointer + chunk)
-  const uint16_t* wsrc[WCH];
-  int wdst[WCH];
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Source byte offsets: block b = wave + 4 i holds tile rows 16 b .. 16 b + 15;
+  // lane l reads row 16 b + l / 4 at chunk (l % 4) ^ ((row / 4) % 4), and
+  // (row / 4) % 4 = (l / 16) % 4.
+  const int rr = lane >> 2;
+  const int gch = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t woff[WB];
 #pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, ch = c & 7;
-    int n, half;
-    if (UPGATE) {
-      half = r >= BN;
-      n = tl.n0 + (half ? r - BN : r);
-    } else {
-      half = 0;
-      n = tl.n0 + r;
-    }
+  for (int i = 0; i < WB; ++i) {
+    const int r = 16 * (wave + 4 * i) + rr;
+    int n = tl.n0 + (UPGATE && r >= BN ? r - BN : r);
     n = n < N ? n : N - 1;
-    wsrc[i] = (UPGATE && half ? W1 : W0) + (int64_t)n * K + ch * 8;
-    wdst[i] = swz(r, ch);
+    woff[i] = ((uint32_t)n * (uint32_t)K + gch * 8) * 2;
   }
-  const uint16_t* xsrc[XCH];
-  int xdst[XCH];
+  uint32_t xoff[XB];
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, ch = c & 7;
-    int row = tl.m0 + r;
+  for (int i = 0; i < XB; ++i) {
+    int row = tl.m0 + 16 * (wave + 4 * i) + rr;
     row = row < tl.m_end ? row : tl.m_end - 1;
-    const int64_t src_row = a.sorted ? (int64_t)a.sorted[row] : (int64_t)row;
-    xsrc[i] = a.tok + src_row * a.ldt + ch * 8;
-    xdst[i] = swz(r, ch);
+    const uint32_t src_row = a.sorted ? (uint32_t)a.sorted[row] : (uint32_t)row;
+    xoff[i] = (src_row * (uint32_t)a.ldt + gch * 8) * 2;
   }
+  // With WB blocks per wave, the first WB/2 hold up rows (tile rows < BN).
+  auto dma = [&](int kt, uint16_t* lw, uint16_t* lx) {
+    const char* bw0 = (const char*)(W0 + kt * BK);
+    if (UPGATE) {
+      dma_tile<WB / 2>(bw0, woff, lw, wave);
+      dma_tile<WB / 2>((const char*)(W1 + kt * BK), woff + WB / 2, lw + 4 * (WB / 2) * 512,
+                       wave);
+    } else {
+      dma_tile<WB>(bw0, woff, lw, wave);
+    }
+    dma_tile<XB>((const char*)(a.tok + kt * BK), xoff, lx, wave);
+  };
 
-  const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % NWN, wm = wave / NWN;
   f32x16 acc[NS][TN][TM];
 #pragma unroll
@@ -129,48 +167,114 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][i][j][r] = 0.f;
 
-  u32x4 rw[WCH], rx[XCH];
-  auto gload = [&](int kt) {
-    const int ko = kt * BK;
+  // Fragment read offsets (elements) of the two k-steps of a slab: row of
+  // sub-tile 0; the other sub-tiles are whole 32-row blocks further.
+  int fxo[2], fwo[2];
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) rw[i] = *(const u32x4*)(wsrc[i] + ko);
+  for (int kk = 0; kk < 2; ++kk) {
+    const int ch = kk * 2 + (lane >> 5);
+    fxo[kk] = swz(wm * WM + (lane & 31), ch);
+    fwo[kk] = swz(wn * WN + (lane & 31), ch);
+  }
+  u32x4 fx0[TM], fw0[NS][TN], fx1[TM], fw1[NS][TN];  // fragments of k-step 0 / 1
+  auto fload = [&](const uint16_t* lw, const uint16_t* lx, int kk, u32x4* fx, u32x4 (*fw)[TN]) {
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) rx[i] = *(const u32x4*)(xsrc[i] + ko);
+    for (int j = 0; j < TM; ++j) fx[j] = *(const u32x4*)(&lx[fxo[kk] + j * 32 * BK]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        fw[s][i] = *(const u32x4*)(&lw[fwo[kk] + (s * BN + i * 32) * BK]);
   };
-  auto lstore = [&](int buf) {
+  auto mfmas = [&](const u32x4* fx, u32x4 (*fw)[TN]) {
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) *(u32x4*)(&lw[buf][wdst[i]]) = rw[i];
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) *(u32x4*)(&lx[buf][xdst[i]]) = rx[i];
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[s][i][j] = mfma32(fw[s][i], fx[j], acc[s][i][j]);
+  };
+  constexpr int NF = TM + NS * TN;   // fragment reads per k-step
+  constexpr int NMF = NS * TN * TM;  // MFMAs per k-step
+  static_assert(NMF >= NF, "pipeline shape");
+  // Issue order for one k-step: one MFMA, then one fragment read (and one DMA
+  // when `dmas`), NF times; the remaining MFMAs last.
+  auto pipeline = [&](bool dmas) {
+#pragma unroll
+    for (int r = 0; r < NF; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (dmas && r < NDMA) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+    if (dmas)
+      for (int r = NF; r < NDMA; ++r) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NF, 0);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Wait until at most n slabs' DMA of this wave are outstanding (and every
+  // fragment read is done), then for all waves.
+  auto wait_slabs = [&](int n) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (n >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA) & kLgkm0);
+    else if (n == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA) & kLgkm0);
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & kLgkm0);
+    barrier();
   };
 
   const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
-      u32x4 fx[TM];
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        fx[j] = *(const u32x4*)(&lx[buf][swz(wm * WM + j * 32 + (lane & 31), ch)]);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const u32x4 fw =
-              *(const u32x4*)(&lw[buf][swz(s * BN + wn * WN + i * 32 + (lane & 31), ch)]);
-#pragma unroll
-          for (int j = 0; j < TM; ++j) acc[s][i][j] = mfma32(fw, fx[j], acc[s][i][j]);
-        }
-      }
+  // The first nk % 4 slabs go through buffer 0 one at a time, so the ring
+  // below always runs a whole number of 4-slab turns.
+  const int r0 = nk & 3;
+  for (int kt = 0; kt < r0; ++kt) {
+    dma(kt, lw0, lx0);
+    wait_slabs(0);
+    fload(lw0, lx0, 0, fx0, fw0);
+    fload(lw0, lx0, 1, fx1, fw1);
+    mfmas(fx0, fw0);
+    mfmas(fx1, fw1);
+    wait_slabs(0);
+  }
+  const int m = nk - r0;
+  if (m > 0) {
+    dma(r0 + 0, lw0, lx0);
+    dma(r0 + 1, lw1, lx1);
+    dma(r0 + 2, lw2, lx2);
+    wait_slabs(2);
+    fload(lw0, lx0, 0, fx0, fw0);
+    // One slab: DMA the slab three ahead into the buffer freed last slab;
+    // k-step 0 MFMAs while reading k-step 1 fragments; wait until the next
+    // slab has landed; k-step 1 MFMAs while reading the next slab's k-step 0.
+    // No branches, so each half is one scheduling region: near the end the
+    // DMA re-fetches the last slab into a buffer nothing reads any more, and
+    // the final next-slab read is simply unused.
+#define MOE_SLAB(J, LWC, LXC, LWN, LXN, LWT, LXT) \
+    {                                             \
+      dma(r0 + min((J) + 3, m - 1), LWT, LXT);    \
+      fload(LWC, LXC, 1, fx1, fw1);               \
+      mfmas(fx0, fw0);                            \
+      pipeline(true);                             \
+      wait_slabs(2);                              \
+      fload(LWN, LXN, 0, fx0, fw0);               \
+      mfmas(fx1, fw1);                            \
+      pipeline(false);                            \
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    for (int j = 0; j < m; j += 4) {
+      MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw3, lx3)
+      MOE_SLAB(j + 1, lw1, lx1, lw2, lx2, lw0, lx0)
+      MOE_SLAB(j + 2, lw2, lx2, lw3, lx3, lw1, lx1)
+      MOE_SLAB(j + 3, lw3, lx3, lw0, lx0, lw2, lx2)
+    }
+#undef MOE_SLAB
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
   }
 
   // D[n = feature][m = row]: lane holds row (lane & 31) and, for q = 0..3,
@@ -314,7 +418,7 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, block, 0, s, u);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 64, 32, true>), grid, block, 0, s,
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 128, 64, true>), grid, block, 0, s,
                      up_args(P, x));
   return hipGetLastError();
 }
@@ -331,7 +435,7 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, block, 0, s, dn);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 64, false>), grid, block, 0, s,
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 128, 128, false>), grid, block, 0, s,
                      down_args(P, x));
   return hipGetLastError();
 }

@@ -8,19 +8,19 @@ namespace moe {
 int row_tile(int kind) {
   switch (kind) {
     case KIND_F32: return 32;
-    default: return 128;
+    default: return 256;
   }
 }
 int up_col_tile(int kind) {
   switch (kind) {
     case KIND_F32: return 32;
-    default: return 64;
+    default: return 128;
   }
 }
 int down_col_tile(int kind) {
   switch (kind) {
     case KIND_F32: return 32;
-    default: return 128;
+    default: return 256;
   }
 }
 

@@ -6,7 +6,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
