@@ -61,7 +61,7 @@ typedef enum moe_status {
 } moe_status;
 
 /* Which expert-GEMM kernels run.  AUTO picks DECODE when the mean number of
- * rows per routed expert, T*k/E, is at most 64, else PREFILL.  MOE_F32 layers
+ * rows per routed expert, T*k/E, is at most 8, else PREFILL.  MOE_F32 layers
  * always use their float32 kernels. */
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2 } moe_path;
 

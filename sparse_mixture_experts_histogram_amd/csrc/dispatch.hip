@@ -28,7 +28,7 @@ constexpr int kDispatchThreads = 1024;
 constexpr int kMaxGroups = kMaxExperts + kMaxShared;
 
 struct TileCfg {
-  int bm, bn, n_tiles;
+  int bm, bn, n_tiles, row_list;
 };
 
 // Inclusive scan of v over the block (kDispatchThreads entries, one per
@@ -57,20 +57,27 @@ __device__ int block_excl_scan(int v, int* buf, int* total) {
 // about 32 tiles that hold every row tile of a few consecutive column tiles
 // (row tile fastest), so the workgroups that run together on one XCD share
 // both the weight tiles and the token tiles through that XCD's L2.
-// tiles[0].g holds the entry count.
+// tiles[0] = {entry count, row tiles, column tiles, 0}.
 __device__ void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
                             TileCfg c, Tile* tiles) {
   const int total = mtot * c.n_tiles;
   if (threadIdx.x == 0) tiles[0] = Tile{total, mtot, c.n_tiles, 0};
-  for (int L = threadIdx.x; L < total; L += blockDim.x) {
-    const int mL = L / c.n_tiles;  // which row tile "slot" (for the group search)
-    int lo = 0, hi = G - 1;        // largest g with mbase[g] <= mL
+  // Row-tile list only: entry 1 + i is row tile i (in group order); a kernel
+  // reads entry L as row tile L % mtot of column tile L / mtot.
+  const int entries = c.row_list ? mtot : total;
+  for (int L = threadIdx.x; L < entries; L += blockDim.x) {
+    const int mL = c.row_list ? L : L / c.n_tiles;  // row tile "slot"
+    int lo = 0, hi = G - 1;  // largest g with mbase[g] <= mL (a non-empty group)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (mbase[mid] <= mL) lo = mid; else hi = mid - 1;
     }
-    // skip empty groups that share the same base
-    int g = lo;
+    const int g = lo;
+    if (c.row_list) {
+      const int m0 = goff[g] + (mL - mbase[g]) * c.bm;
+      tiles[1 + L] = Tile{g, m0, min(m0 + c.bm, goff[g] + gsize[g]), 0};
+      continue;
+    }
     const int Mg = (gsize[g] + c.bm - 1) / c.bm;
     const int local = L - mbase[g] * c.n_tiles;
     const int sn = Mg >= 32 ? 1 : 32 / Mg;
@@ -192,7 +199,9 @@ __global__ __launch_bounds__(kDispatchThreads) void tiles_kernel(const int32_t* 
   build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down);
 }
 
-static TileCfg tile_cfg(const GemmShape& s) { return TileCfg{s.bm, s.bn, s.n_tiles}; }
+static TileCfg tile_cfg(const GemmShape& s) {
+  return TileCfg{s.bm, s.bn, s.n_tiles, s.row_list ? 1 : 0};
+}
 
 hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,
                            const int32_t* blk_rank, int32_t* counts, int32_t* offsets,

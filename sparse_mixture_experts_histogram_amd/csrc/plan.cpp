@@ -5,23 +5,24 @@
 
 namespace moe {
 
-int row_tile(int kind) {
-  switch (kind) {
-    case KIND_F32: return 32;
-    default: return 256;
-  }
+// Tile shapes (rows per tile, output columns per tile) of the two grouped
+// GEMMs for each kernel family; they must match the kernel instantiations
+// launched in experts.hip.  Prefill uses 256-row tiles when experts average
+// at least 384 rows (less padding is then worth the larger reuse), else 128.
+static int prefill_rows(const moe_desc* d) {
+  return d->T * d->k >= 384LL * d->E ? 256 : 128;
+}
+int up_row_tile(int kind, const moe_desc* d) {
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : 32;
 }
 int up_col_tile(int kind) {
-  switch (kind) {
-    case KIND_F32: return 32;
-    default: return 128;
-  }
+  return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_BF16_DECODE ? 16 : 32;
+}
+int down_row_tile(int kind, const moe_desc* d) {
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : 32;
 }
 int down_col_tile(int kind) {
-  switch (kind) {
-    case KIND_F32: return 32;
-    default: return 256;
-  }
+  return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -58,7 +59,7 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.nblk = cdiv(T, kRouterTokens);
   P.ffn_max = d->n_shared > 0 ? std::max(d->ffn, d->ffn_shared) : d->ffn;
   if (d->path == MOE_PATH_AUTO)
-    P.path = (T * d->k <= 64LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    P.path = (T * d->k <= 8LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   else
     P.path = d->path;
   if (d->dtype == MOE_F32)
@@ -66,21 +67,22 @@ int make_plan(const moe_desc* d, Plan* p) {
   else
     P.kind = P.path == MOE_PATH_DECODE ? KIND_BF16_DECODE : KIND_BF16_PREFILL;
 
-  const int bm = row_tile(P.kind);
   const int64_t nz = std::min<int64_t>(d->E, P.pairs);
-  P.max_row_tiles = (P.pairs + nz * (bm - 1)) / bm + d->n_shared * cdiv(T, bm);
-  auto shape = [&](int bn, int ncols, int ncols_sh) {
+  auto shape = [&](int bm, int bn, int ncols, int ncols_sh) {
     GemmShape s{};
     s.bm = bm;
     s.bn = bn;
     s.n_cols = ncols;
     s.n_cols_shared = d->n_shared > 0 ? ncols_sh : ncols;
     s.n_tiles = (int)cdiv(std::max(s.n_cols, s.n_cols_shared), bn);
-    s.max_tiles = P.max_row_tiles * s.n_tiles;
+    s.max_row_tiles = (P.pairs + nz * (bm - 1)) / bm + d->n_shared * cdiv(T, bm);
+    s.max_tiles = s.max_row_tiles * s.n_tiles;
     return s;
   };
-  P.up = shape(up_col_tile(P.kind), d->ffn, d->ffn_shared);
-  P.down = shape(down_col_tile(P.kind), d->d, d->d);
+  P.up = shape(up_row_tile(P.kind, d), up_col_tile(P.kind), d->ffn, d->ffn_shared);
+  P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind), d->d, d->d);
+  // the decode kernels walk a compact list of row tiles (see dispatch.hip)
+  P.up.row_list = P.down.row_list = P.kind == KIND_BF16_DECODE;
 
   const size_t A = 256;
   const size_t eb = d->dtype == MOE_BF16 ? 2 : 4;

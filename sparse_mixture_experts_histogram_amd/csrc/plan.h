@@ -20,6 +20,7 @@ constexpr int kMaxShared = 8;
 constexpr int kRowSlack = 256;
 
 // One GEMM tile: rows [m0, m_end) of group g, output columns [n0, n0 + BN).
+// Entry 0 of a schedule is a header: {entries, row tiles, column tiles, 0}.
 struct Tile {
   int32_t g, m0, m_end, n0;
 };
@@ -30,8 +31,10 @@ struct GemmShape {
   int bn;      // output columns per tile
   int n_cols;  // output columns of a routed group (ffn for up/gate, d for down)
   int n_cols_shared;
-  int n_tiles;         // column tiles of the widest group
-  int64_t max_tiles;   // upper bound of (row tile, column tile) pairs
+  int n_tiles;            // column tiles of the widest group
+  int64_t max_row_tiles;  // upper bound of row tiles over all groups
+  int64_t max_tiles;      // upper bound of (row tile, column tile) pairs
+  bool row_list;          // schedule lists row tiles only (column tile = L / rows)
 };
 
 struct Plan {
@@ -44,7 +47,6 @@ struct Plan {
   int ffn_max;       // max(ffn, ffn_shared)
   int kind;          // kernel family, see KernelKind
   GemmShape up, down;
-  int64_t max_row_tiles;
   // workspace byte offsets
   size_t o_blk_hist, o_blk_rank, o_counts, o_offsets, o_tiles_up, o_tiles_down, o_sorted,
       o_slot, o_idx, o_w, o_h, o_out, total;
@@ -55,9 +57,10 @@ enum KernelKind { KIND_F32 = 0, KIND_BF16_PREFILL = 1, KIND_BF16_DECODE = 2 };
 // Fill `p` for `d`; returns a moe_status.
 int make_plan(const moe_desc* d, Plan* p);
 
-// Column-tile counts and tile-shape choices (shared with the kernels' launch code).
-int row_tile(int kind);
+// Tile shapes of the grouped GEMMs per kernel family.
+int up_row_tile(int kind, const moe_desc* d);
 int up_col_tile(int kind);
+int down_row_tile(int kind, const moe_desc* d);
 int down_col_tile(int kind);
 
 }  // namespace moe

@@ -9,8 +9,8 @@
 //
 // One workgroup (4 waves) owns kRouterTokens tokens and every expert.  The
 // bf16 variant computes the logit tile with 16x16x32 bf16 MFMAs (exact bf16
-// products, fp32 accumulation); when E is small the K range is split across
-// waves and the partial tiles are summed in a fixed order.  Selection runs one
+// products, fp32 accumulation); the K range is split across waves when E
+// leaves room for it and the partial tiles are summed in a fixed order.  Selection runs one
 // wave per token on 64-bit keys (order-preserving fp32 logit, then 2^32-1-e),
 // so a wave-wide max picks the largest logit and, among exact ties, the lowest
 // expert index.  Only the kept logits are needed for the weights:
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   const int ld = etiles * 16 + 4;
   float* lg = lds;
   int32_t* sel = (int32_t*)(lds + KS * kRouterTokens * ld);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kRouterTokens;
   const int ks = wave % KS, tg = wave / KS, tstep = 4 / KS;
 
@@ -138,18 +138,32 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     wp[i] = wr + (int64_t)e * d + (lane >> 4) * 8;
     acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // K loop in batches of U k-steps: all loads of a batch are issued before
+  // its MFMAs, so each wave keeps U*(NT+1) 16-byte loads per lane in flight.
+  // Tiles past the last expert read a clamped row and are not stored.
+  constexpr int U = 4;
   const int nk = d >> 5;
   const int c0 = ks * nk / KS, c1 = (ks + 1) * nk / KS;
-#pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
+  int c = c0;
+  for (; c + U <= c1; c += U) {
+    u32x4 a[U], b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = *(const u32x4*)(xp + (c + u) * 32);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) b[u][i] = *(const u32x4*)(wp[i] + (c + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] = mfma16(a[u], b[u][i], acc[i]);
+    __builtin_amdgcn_sched_group_barrier(0x020, U * (NT + 1), 0);  // every load first
+    __builtin_amdgcn_sched_group_barrier(0x008, U * NT, 0);        // then the MFMAs
+  }
+  for (; c < c1; ++c) {
     const u32x4 a = *(const u32x4*)(xp + c * 32);
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if (tg + i * tstep < etiles) {
-        const u32x4 b = *(const u32x4*)(wp[i] + c * 32);
-        acc[i] = mfma16(a, b, acc[i]);
-      }
-    }
+    for (int i = 0; i < NT; ++i) acc[i] = mfma16(a, *(const u32x4*)(wp[i] + c * 32), acc[i]);
   }
   // D[m = token][n = expert]: lane holds expert (lane & 15), tokens 4*(lane>>4)+r
 #pragma unroll
@@ -227,8 +241,11 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
                        blk_rank);
     return hipGetLastError();
   }
+  // Split K over the 4 waves as far as the per-wave tile count allows (at
+  // most 8 tiles of 16 experts per wave): small token counts then still have
+  // all four waves streaming the router matrix.
   const int etiles = (D.E + 15) / 16;
-  const int KS = etiles == 1 ? 4 : etiles == 2 ? 2 : 1;
+  const int KS = etiles <= 8 ? 4 : etiles <= 16 ? 2 : 1;
   const int nt = (etiles + (4 / KS) - 1) / (4 / KS);
   const size_t lds = (size_t)KS * kRouterTokens * (etiles * 16 + 4) * 4 + sel_bytes;
   auto args = [&](auto kern) {

@@ -67,7 +67,8 @@ def test_workspace_and_paths():
     assert ws > (R * 14336 * 2 + R * 4096 * 4)
     assert moe.moe_resolve_path(d) == "prefill"
     assert moe.moe_resolve_path(desc(T=16, d=4096, E=8, k=2, ffn=14336)) == "decode"
-    assert moe.moe_resolve_path(desc(T=512, d=2880, E=128, k=4, ffn=2880)) == "decode"
+    assert moe.moe_resolve_path(desc(T=128, d=2880, E=128, k=4, ffn=2880)) == "decode"
+    assert moe.moe_resolve_path(desc(T=512, d=2880, E=128, k=4, ffn=2880)) == "prefill"
     assert moe.moe_resolve_path(desc(T=4096, d=7168, E=256, k=8, ffn=2048, n_shared=1,
                                      ffn_shared=2048)) == "prefill"
     assert moe.moe_grouped_rows(desc(T=10, k=3, n_shared=2, ffn_shared=64)) == 50

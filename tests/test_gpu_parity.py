@@ -36,6 +36,8 @@ SMALL = {c.name: c for c in [
     custom("f32_shared", 110, T=70, d=64, E=5, k=3, ffn=36, n_shared=1, ffn_shared=52,
            dtype="f32"),
     custom("one_token", 111, T=1, d=128, E=8, k=2, ffn=128),
+    # >= 384 rows per expert: the 256-row prefill tiles, ragged last tiles
+    custom("rows256", 112, T=900, d=192, E=2, k=1, ffn=320),
     NAMED["tiny_f32"],
 ]}
 
