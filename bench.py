@@ -40,8 +40,14 @@ def parse():
     ap.add_argument("--decode-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the T=16 decode leg")
-    ap.add_argument("--cpu-sample", type=int, default=1024,
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the timed T=4096 steps (profiling the decode leg alone)")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MB",
+                    help="also run one plain device copy of MB megabytes (a kernel of known "
+                         "traffic, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle runs (median taken)")
     return ap.parse_args()
 
 
@@ -142,9 +148,32 @@ def decode_leg(cfg, x, W, k, iters):
     return dec
 
 
-def cpu_baseline(cfg, li, sample):
+def kernel_source_hash() -> str:
+    """Hash of the expert-GEMM kernel source the library was built from."""
+    import hashlib
+    p = os.path.join(ROOT, "sparse_mixture_experts_histogram_amd", "csrc", "experts.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(key):
+    """HBM bytes per launch of a kernel from the stored rocprofv3 counter
+    record (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
+    None when the record is missing or was taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("experts_hip_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, li, sample, reps):
     """The fp64 oracle as written, on the first `sample` tokens of the same
-    workload (routing and every chosen expert for those tokens)."""
+    workload (routing and every chosen expert), median of `reps` runs."""
     import oracle
     from moe_inputs import generate
     try:
@@ -153,15 +182,19 @@ def cpu_baseline(cfg, li, sample):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     xs = li.x[:sample]
-    # draw the weights outside the timed region (they are inputs, resident)
+    # the weights are inputs: drawn outside the timed region
     wts = {e: generate.expert_weights(cfg, e) for e in range(cfg.E)}
-    t0 = time.perf_counter()
-    oracle.moe_forward(xs, li.w_router, li.bias, cfg.k, lambda e: wts[e], cfg.E, cfg.dtype)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.moe_forward(xs, li.w_router, li.bias, cfg.k, lambda e: wts[e], cfg.E, cfg.dtype)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {sample} tokens of the {cfg.name} T={cfg.T} workload, fp64 numpy "
-                      f"oracle (routing + chosen experts), {dt:.1f} s"}
+            "sample": f"first {sample} tokens of the {cfg.name} T={cfg.T} workload (routing + "
+                      f"chosen experts), fp64 numpy oracle, median of {reps} runs of "
+                      f"{dt:.2f} s each ({sum(times):.1f} s total)"}
 
 
 def main():
@@ -183,6 +216,19 @@ def main():
     print(f"[bench] inputs ready in {time.perf_counter() - t_in:.1f}s", file=sys.stderr,
           flush=True)
 
+    if args.copy_check:
+        # one elementwise kernel that reads and writes exactly MB megabytes
+        n = args.copy_check * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.no_prefill:
+        dec = decode_leg(cfg, x, W, k, args.decode_iters)
+        print(json.dumps({"decode_only": dec}), flush=True)
+        return
     wall, layer, per, counts = time_forward(x, W, k, args.steps, args.warmup)
     print(f"[bench] prefill: {wall * 1e3:.3f} ms/step wall, per-kernel ms {per}",
           file=sys.stderr, flush=True)
@@ -200,7 +246,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, li, args.cpu_sample)
+        cpu = cpu_baseline(cfg, li, args.cpu_sample, args.cpu_reps)
         print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
 
     line = {
@@ -213,7 +259,8 @@ def main():
                    "y": "fp32", "path": "prefill", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "expert_up (grouped up/gate GEMM + SwiGLU)",
                      "achieved": round(up_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(up_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(up_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic("expert_up_mixtral_t4096"),
                      "avg_launch_ms": round(per["expert_up"], 4),
                      "algorithmic_flops_per_launch": flops_up},
         "grouped_gemm_frac_mfma": round(gemm_tf / PEAK_BF16_TFLOPS, 4),

@@ -28,7 +28,7 @@ constexpr int kDispatchThreads = 1024;
 constexpr int kMaxGroups = kMaxExperts + kMaxShared;
 
 struct TileCfg {
-  int bm, bn, n_tiles, row_list;
+  int bm, bn, n_tiles, row_list, n_fastest;
 };
 
 // Inclusive scan of v over the block (kDispatchThreads entries, one per
@@ -83,8 +83,9 @@ __device__ void build_tiles(const int* goff, const int* gsize, const int* mbase,
     const int sn = Mg >= 32 ? 1 : 32 / Mg;
     const int chunk = local / (Mg * sn);
     const int within = local - chunk * Mg * sn;
-    const int mt = within % Mg;
-    const int nt = chunk * sn + within / Mg;
+    const int nin = min(sn, c.n_tiles - chunk * sn);  // column tiles in this chunk
+    const int mt = c.n_fastest ? within / nin : within % Mg;
+    const int nt = chunk * sn + (c.n_fastest ? within % nin : within / Mg);
     const int m0 = goff[g] + mt * c.bm;
     const int mend = min(m0 + c.bm, goff[g] + gsize[g]);
     tiles[1 + L] = Tile{g, m0, mend, nt * c.bn};
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kDispatchThreads) void tiles_kernel(const int32_t* 
 }
 
 static TileCfg tile_cfg(const GemmShape& s) {
-  return TileCfg{s.bm, s.bn, s.n_tiles, s.row_list ? 1 : 0};
+  return TileCfg{s.bm, s.bn, s.n_tiles, s.row_list ? 1 : 0, s.n_fastest};
 }
 
 hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,

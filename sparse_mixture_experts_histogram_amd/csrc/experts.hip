@@ -41,6 +41,7 @@ struct GemmArgs {
   void* out;                  // h (bf16, up/gate) or out (fp32, down)
   int ldo;                    // row stride of out, elements
   const Tile* tiles;
+  int xcd_remap;              // 1: consecutive schedule entries run on one XCD
 };
 
 constexpr int BK = 32;  // K slab: 4 chunks of 8 bf16 per tile row (64 bytes)
@@ -58,11 +59,15 @@ __device__ __forceinline__ Tile uniform_tile(const Tile& t) {
               __builtin_amdgcn_readfirstlane(t.m_end), __builtin_amdgcn_readfirstlane(t.n0)};
 }
 
-// Remap the workgroup index so consecutive tile-list entries share an XCD.
-__device__ __forceinline__ int tile_of_block(const Tile* tiles) {
+// Schedule entry of this workgroup.  With `remap`, consecutive entries run on
+// one XCD (the dispatcher deals workgroup i to XCD i % 8), so the workgroups
+// that share weight and token tiles share that XCD's L2; without it, entries
+// are spread over all XCDs.
+__device__ __forceinline__ int tile_of_block(const Tile* tiles, int remap = 1) {
   const int count = tiles[0].g;
-  const int per = (count + 7) >> 3;
   const int bid = blockIdx.x;
+  if (!remap) return bid < count ? bid : -1;
+  const int per = (count + 7) >> 3;
   if (bid >= per * 8) return -1;
   const int L = (bid & 7) * per + (bid >> 3);
   return L < count ? L : -1;
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
 
-  const int L = tile_of_block(a.tiles);
+  const int L = tile_of_block(a.tiles, a.xcd_remap);
   if (L < 0) return;
   const Tile tl = uniform_tile(a.tiles[1 + L]);
   const bool sh = tl.g >= a.E;
@@ -519,14 +524,14 @@ static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
   return GemmArgs{(const uint16_t*)x.x, x.sorted_token, D.d, (const uint16_t*)x.w_up,
                   (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
                   (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
-                  x.tiles_up};
+                  x.tiles_up, P.up.xcd_remap};
 }
 static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
   const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
   return GemmArgs{(const uint16_t*)x.h, nullptr, P.ffn_max, (const uint16_t*)x.w_down, nullptr,
                   (const uint16_t*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
-                  x.tiles_down};
+                  x.tiles_down, P.down.xcd_remap};
 }
 
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {

@@ -83,6 +83,14 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind), d->d, d->d);
   // the decode kernels walk a compact list of row tiles (see dispatch.hip)
   P.up.row_list = P.down.row_list = P.kind == KIND_BF16_DECODE;
+  // Schedule order (measured on MI355X): the up/gate GEMM runs chunks of
+  // consecutive entries (row tile fastest) per XCD; the down GEMM (long K, few
+  // column tiles) is faster with column tile fastest and its entries spread
+  // over all XCDs.
+  P.up.n_fastest = 0;
+  P.up.xcd_remap = 1;
+  P.down.n_fastest = 1;
+  P.down.xcd_remap = 0;
 
   const size_t A = 256;
   const size_t eb = d->dtype == MOE_BF16 ? 2 : 4;

@@ -35,6 +35,8 @@ struct GemmShape {
   int64_t max_row_tiles;  // upper bound of row tiles over all groups
   int64_t max_tiles;      // upper bound of (row tile, column tile) pairs
   bool row_list;          // schedule lists row tiles only (column tile = L / rows)
+  int n_fastest;          // within a schedule chunk: 0 = row tile fastest, 1 = column
+  int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
 };
 
 struct Plan {
