@@ -78,7 +78,8 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
   Tile* td = W.at<Tile>(P.o_tiles_down);
   float* out = W.at<float>(P.o_out);
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
-               W.at<void>(P.o_h), out};
+               W.at<void>(P.o_h), out, P.down.ksplit};
+  const int64_t part_stride = ((int64_t)P.R + kRowSlack) * d->d;
   MOE_TRY(mark(0));
   MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank, s));
   MOE_TRY(mark(1));
@@ -88,7 +89,7 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
   MOE_TRY(mark(3));
   MOE_TRY(launch_expert_down(P, a, s));
   MOE_TRY(mark(4));
-  MOE_TRY(launch_combine(P, out, w, slot, offsets, y, s));
+  MOE_TRY(launch_combine(P, out, P.down.ksplit, part_stride, w, slot, offsets, y, s));
   MOE_TRY(mark(5));
   return MOE_OK;
 }
@@ -173,7 +174,7 @@ int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* 
   Tile* td = W.at<Tile>(P.o_tiles_down);
   MOE_TRY(launch_tiles(P, group_offsets, tu, td, s));
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted_token, tu, td,
-               W.at<void>(P.o_h), expert_out};
+               W.at<void>(P.o_h), expert_out, 1};
   MOE_TRY(launch_expert_up(P, a, s));
   MOE_TRY(launch_expert_down(P, a, s));
   return MOE_OK;
@@ -186,7 +187,7 @@ int moe_combine(const moe_desc* d, const float* expert_out, const float* topk_w,
   int st = make_plan(d, &P);
   if (st != MOE_OK || d->T == 0) return st;
   if (!expert_out || !topk_w || !slot_row || !group_offsets || !y) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(launch_combine(P, expert_out, topk_w, slot_row, group_offsets, y,
+  MOE_TRY(launch_combine(P, expert_out, 1, 0, topk_w, slot_row, group_offsets, y,
                          (hipStream_t)stream));
   return MOE_OK;
 }

@@ -4,15 +4,18 @@
 // and VRAM"; shared experts added with weight one per page "Mixture of Experts
 // (MoE): routing, expert parallelism, and memory", section "Shared
 // experts").  A gather per token, no atomics, so the result is deterministic.
-// HBM-bound: it reads (k + n_shared) float32 rows and writes one row per
-// token; each workgroup handles one token with 16-byte accesses.
+// When the down GEMM split K in two, each expert output row is the sum of its
+// two partial rows, added here in a fixed order.
+// HBM-bound: it reads (k + n_shared) float32 rows (per K part) and writes one
+// row per token; each workgroup handles one token with 16-byte accesses.
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <bool Y_BF16>
+template <bool Y_BF16, int NP>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
+                                                      int64_t part_stride,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_row,
                                                       const int32_t* __restrict__ offsets, int d,
@@ -27,11 +30,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     rows[threadIdx.x] = offsets[E + threadIdx.x - k] + t;
   }
   __syncthreads();
+  // expert output row r: its NP partial K-range sums, added in order
+  auto row4 = [&](int r, int c) {
+    float4 v = ((const float4*)(out + (int64_t)r * d))[c];
+#pragma unroll
+    for (int q = 1; q < NP; ++q) {
+      const float4 u = ((const float4*)(out + q * part_stride + (int64_t)r * d))[c];
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    return v;
+  };
   const int d4 = d >> 2;
   for (int c = threadIdx.x; c < d4; c += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
-      const float4 v = ((const float4*)(out + (int64_t)rows[j] * d))[c];
+      const float4 v = row4(rows[j], c);
       const float wj = wts[j];
       acc.x = fmaf(wj, v.x, acc.x);
       acc.y = fmaf(wj, v.y, acc.y);
@@ -39,7 +55,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc.w = fmaf(wj, v.w, acc.w);
     }
     for (int s = 0; s < n_sh; ++s) {
-      const float4 v = ((const float4*)(out + (int64_t)rows[k + s] * d))[c];
+      const float4 v = row4(rows[k + s], c);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -56,16 +72,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const Plan& P, const float* out, const float* w, const int32_t* slot_row,
-                          const int32_t* offsets, void* y, hipStream_t s) {
+hipError_t launch_combine(const Plan& P, const float* out, int nparts, int64_t part_stride,
+                          const float* w, const int32_t* slot_row, const int32_t* offsets,
+                          void* y, hipStream_t s) {
   const moe_desc& D = P.desc;
   const dim3 grid((unsigned)D.T), block(256);
-  if (D.y_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, out, w, slot_row, offsets, D.d,
-                       D.k, D.E, D.n_shared, y);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, out, part_stride, w, slot_row, offsets, D.d, D.k,
+                       D.E, D.n_shared, y);
+  };
+  const bool bf = D.y_dtype == MOE_BF16;
+  if (nparts == 2)
+    bf ? go(combine_kernel<true, 2>) : go(combine_kernel<false, 2>);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, out, w, slot_row, offsets, D.d,
-                       D.k, D.E, D.n_shared, y);
+    bf ? go(combine_kernel<true, 1>) : go(combine_kernel<false, 1>);
   return hipGetLastError();
 }
 

@@ -42,6 +42,8 @@ struct GemmArgs {
   int ldo;                    // row stride of out, elements
   const Tile* tiles;
   int xcd_remap;              // 1: consecutive schedule entries run on one XCD
+  int ksplit;                 // K ranges per tile (partial sums to separate outputs)
+  int64_t split_stride;       // elements between the outputs of consecutive K ranges
 };
 
 constexpr int BK = 32;  // K slab: 4 chunks of 8 bf16 per tile row (64 bytes)
@@ -106,8 +108,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
 
-  const int L = tile_of_block(a.tiles, a.xcd_remap);
-  if (L < 0) return;
+  // With a K split, workgroup slots [q*count, (q+1)*count) run K range q of
+  // every tile and write their partial sums to output q.
+  int L, split = 0;
+  if (a.ksplit > 1) {
+    const int count = a.tiles[0].g;
+    const int bid = blockIdx.x;
+    if (bid >= count * a.ksplit) return;
+    split = bid / count;
+    L = bid - split * count;
+  } else {
+    L = tile_of_block(a.tiles, a.xcd_remap);
+    if (L < 0) return;
+  }
   const Tile tl = uniform_tile(a.tiles[1 + L]);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
@@ -149,7 +162,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     xoff[i] = (src_row * (uint32_t)a.ldt + gch * 8) * 2;
   }
   // With WB blocks per wave, the first WB/2 hold up rows (tile rows < BN).
-  auto dma = [&](int kt, uint16_t* lw, uint16_t* lx) {
+  const int nk_all = K / BK;
+  const int kb = split * nk_all / a.ksplit;  // first slab of this K range
+  auto dma = [&](int kt_local, uint16_t* lw, uint16_t* lx) {
+    const int kt = kb + kt_local;
     const char* bw0 = (const char*)(W0 + kt * BK);
     if (UPGATE) {
       dma_tile<WB / 2>(bw0, woff, lw, wave);
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     barrier();
   };
 
-  const int nk = K / BK;
+  const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
   // The first nk % 4 slabs go through buffer 0 one at a time, so the ring
   // below always runs a whole number of 4-slab turns.
   const int r0 = nk & 3;
@@ -309,7 +325,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           v.y = acc[0][i][j][4 * q + 1];
           v.z = acc[0][i][j][4 * q + 2];
           v.w = acc[0][i][j][4 * q + 3];
-          *(float4*)((float*)a.out + (int64_t)row * a.ldo + n) = v;
+          *(float4*)((float*)a.out + split * a.split_stride + (int64_t)row * a.ldo + n) = v;
         }
       }
     }
@@ -524,14 +540,15 @@ static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
   return GemmArgs{(const uint16_t*)x.x, x.sorted_token, D.d, (const uint16_t*)x.w_up,
                   (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
                   (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
-                  x.tiles_up, P.up.xcd_remap};
+                  x.tiles_up, P.up.xcd_remap, 1, 0};
 }
 static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
   const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
   return GemmArgs{(const uint16_t*)x.h, nullptr, P.ffn_max, (const uint16_t*)x.w_down, nullptr,
                   (const uint16_t*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
-                  x.tiles_down, P.down.xcd_remap};
+                  x.tiles_down, P.down.xcd_remap, x.ksplit,
+                  (int64_t)((size_t)P.R + kRowSlack) * D.d};
 }
 
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
@@ -560,7 +577,7 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
 hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   const moe_desc& D = P.desc;
   const dim3 block(256);
-  const dim3 grid((unsigned)(((P.down.max_tiles + 7) / 8) * 8));
+  const dim3 grid((unsigned)(((P.down.max_tiles * x.ksplit + 7) / 8) * 8));
   if (P.kind == KIND_F32) {
     const int ffn_s = D.n_shared ? D.ffn_shared : D.ffn;
     GemmArgsF32 dn{(const float*)x.h, nullptr, P.ffn_max, (const float*)x.w_down, nullptr,

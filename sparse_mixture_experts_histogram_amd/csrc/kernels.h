@@ -36,7 +36,9 @@ struct ExpertArgs {
   const Tile* tiles_up;
   const Tile* tiles_down;
   void* h;
-  float* out;
+  float* out;     // expert outputs; with ksplit > 1, ksplit partial buffers of
+                  // (R + kRowSlack) rows each, summed by the combine
+  int ksplit;     // K ranges of the down GEMM (1 = direct result)
 };
 
 // Grouped up/gate GEMM + SwiGLU (writes h).
@@ -44,8 +46,10 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& a, hipStream_t s);
 // Grouped down GEMM (reads h, writes out).
 hipError_t launch_expert_down(const Plan& P, const ExpertArgs& a, hipStream_t s);
 
-// y[t] = sum_j w[t,j] out[slot_row[t,j]] + sum_s out[offsets[E+s]+t].
-hipError_t launch_combine(const Plan& P, const float* out, const float* w, const int32_t* slot_row,
-                          const int32_t* offsets, void* y, hipStream_t s);
+// y[t] = sum_j w[t,j] out[slot_row[t,j]] + sum_s out[offsets[E+s]+t], where
+// out[r] is the sum of `nparts` partial buffers `part_stride` floats apart.
+hipError_t launch_combine(const Plan& P, const float* out, int nparts, int64_t part_stride,
+                          const float* w, const int32_t* slot_row, const int32_t* offsets,
+                          void* y, hipStream_t s);
 
 }  // namespace moe

@@ -37,6 +37,7 @@ struct GemmShape {
   bool row_list;          // schedule lists row tiles only (column tile = L / rows)
   int n_fastest;          // within a schedule chunk: 0 = row tile fastest, 1 = column
   int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
+  int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
 };
 
 struct Plan {

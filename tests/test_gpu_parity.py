@@ -38,6 +38,8 @@ SMALL = {c.name: c for c in [
     custom("one_token", 111, T=1, d=128, E=8, k=2, ffn=128),
     # >= 384 rows per expert: the 256-row prefill tiles, ragged last tiles
     custom("rows256", 112, T=900, d=192, E=2, k=1, ffn=320),
+    # long K and few tiles: the down GEMM splits K in two (partials summed in the combine)
+    custom("ksplit", 113, T=200, d=128, E=3, k=2, ffn=8192),
     NAMED["tiny_f32"],
 ]}
 
