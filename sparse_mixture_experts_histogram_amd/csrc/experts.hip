@@ -333,23 +333,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- decode
-// Streaming variant for a few rows per group (decode-sized batches), where the
-// layer is bound by reading the touched experts' weights once from HBM.
-// A tile is 16 output features (up/gate: 16 up rows and 16 gate rows) by up
-// to 32 grouped rows; the four waves split K and keep 8 k-steps of 16-byte
-// weight loads per lane in flight.  Weights are read with non-temporal loads
-// (each is used by this tile only; streaming reads measured ~7.0 TB/s that way
-// against ~6.1 TB/s for cached loads); their partial sums are added in LDS in
-// wave order (deterministic).  16x16x32 bf16 MFMAs with the weight rows as
+// Streaming kernel for a few rows per group (decode-sized batches), where the
+// layer is bound by reading the touched experts' weights once from HBM.  A
+// tile is 16 output features (up/gate: 16 up rows and 16 gate rows) by 16
+// grouped rows.  The four waves split K; each copies its K range in 1 KB
+// bursts (8 rows x 64 k: whole 128-byte lines) with global_load_lds_dwordx4
+// into a ring of D LDS stages of its own, D - 1 slabs of 64 k ahead, and reads
+// MFMA fragments from there.  A wave only reads what it fetched itself, so no
+// workgroup barrier is needed until the cross-wave sum, which is added in
+// wave order (deterministic).  Weight bursts are non-temporal (each weight is
+// used by one tile only; the token rows, shared by all column tiles of a
+// group, stay cached).  Measured on MI355X with a 2-stage ring: the Mixtral-
+// shaped 16-token layer's expert GEMMs stream 6.6 TB/s; deeper rings were
+// slower (fewer workgroups per CU), cached weight bursts ~20% slower.
+// Rows of a 1 KB block are 128 bytes; the 16-byte chunk c of row r sits at
+// slot c ^ ((r / 2) % 8), so the 16 lanes of a ds_read_b128 phase (16 rows,
+// one chunk) hit distinct banks.  16x16x32 bf16 MFMAs take the weight rows as
 // the A operand, so a lane ends with 4 consecutive features of one row.
-template <bool UPGATE>
+constexpr int kWeightPolicy = 2;  // cache policy of the weight bursts: nt
+template <bool UPGATE, int D>
 __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(GemmArgs a) {
-  constexpr int BN = 16, MT = 2;                 // features, 16-row m-tiles
-  constexpr int NS = UPGATE ? 2 : 1;
-  constexpr int U = 8;                           // k-steps per load batch
+  constexpr int BN = 16, NS = UPGATE ? 2 : 1;
+  constexpr int WBLK = NS * 2, XBLK = 2;         // 1 KB blocks per slab
+  constexpr int NDMA = WBLK + XBLK;
+  constexpr int SLAB = NDMA * 512;               // bf16 elements per slab
+  static_assert((D - 1) * NDMA <= 63, "vmcnt range");
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
-  // row-tile list: entry L is row tile L % rows of column tile L / rows
   const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
   Tile tl = uniform_tile(a.tiles[1 + L % mtot]);
   tl.n0 = (L / mtot) * BN;
@@ -360,98 +370,98 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(GemmArgs a) {
   const int64_t wstride = (int64_t)N * K;
   const uint16_t* W0 = sh ? a.s0 + (tl.g - a.E) * wstride : a.w0 + tl.g * wstride;
   const uint16_t* W1 = UPGATE ? (sh ? a.s1 + (tl.g - a.E) * wstride : a.w1 + tl.g * wstride)
-                              : nullptr;
-  __shared__ f32x4 red[3][NS][MT][64];
+                              : W0;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4][D][SLAB];
+  static_assert(NS * 64 * sizeof(f32x4) <= SLAB * sizeof(uint16_t), "partial sums fit a stage");
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int koff = (lane >> 4) * 8;  // this lane's 8 k-values within a 32-wide k-step
-  int n = tl.n0 + (lane & 15);
-  n = n < N ? n : N - 1;
-  const uint16_t* wp[NS];
-  wp[0] = W0 + (int64_t)n * K + koff;
-  if (UPGATE) wp[NS - 1] = W1 + (int64_t)n * K + koff;
-  const int rows = tl.m_end - tl.m0;
-  const int nmt = rows > 16 ? 2 : 1;  // m-tiles with at least one row
-  const uint16_t* tp[MT];
+  // this lane's source in each 1 KB block: row 8 b + lane / 8 of the tile, at
+  // the global chunk that lands in slot lane % 8
+  const uint16_t* src[NDMA];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    int row = tl.m0 + t * 16 + (lane & 15);
-    row = row < tl.m_end ? row : tl.m_end - 1;
-    const int64_t src = a.sorted ? (int64_t)a.sorted[row] : (int64_t)row;
-    tp[t] = a.tok + src * a.ldt + koff;
-  }
-  f32x4 acc[NS][MT];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = K >> 5;
-  const int k0 = wave * nks / 4, k1 = (wave + 1) * nks / 4;
-  int ks = k0;
-  for (; ks + U <= k1; ks += U) {
-    u32x4 fw[U][NS], fx[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        fw[u][s] = __builtin_nontemporal_load((const u32x4*)(wp[s] + (ks + u) * 32));
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        if (t < nmt) fx[u][t] = *(const u32x4*)(tp[t] + (ks + u) * 32);
+  for (int b = 0; b < NDMA; ++b) {
+    const int r = 8 * b + (lane >> 3);
+    const int gch = (lane & 7) ^ ((r >> 1) & 7);
+    if (b < WBLK) {
+      int n = tl.n0 + (r & 15);
+      n = n < N ? n : N - 1;
+      src[b] = (UPGATE && b >= 2 ? W1 : W0) + (int64_t)n * K + gch * 8;
+    } else {
+      int row = tl.m0 + (r & 15);
+      row = row < tl.m_end ? row : tl.m_end - 1;
+      const int64_t t = a.sorted ? (int64_t)a.sorted[row] : (int64_t)row;
+      src[b] = a.tok + t * a.ldt + gch * 8;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        if (t < nmt)
-#pragma unroll
-          for (int s = 0; s < NS; ++s) acc[s][t] = mfma16(fw[u][s], fx[u][t], acc[s][t]);
   }
-  for (; ks < k1; ++ks) {
+  const int nsl = K >> 6;
+  const int s0 = wave * nsl / 4, s1 = (wave + 1) * nsl / 4, n = s1 - s0;
+  auto dma = [&](int sl, uint16_t* dst) {
+    sl = min(sl, s1 - 1);  // past the end: re-fetch the last slab into a dead stage
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      if (t < nmt) {
-        const u32x4 fx = *(const u32x4*)(tp[t] + ks * 32);
+    for (int b = 0; b < WBLK; ++b)
+      __builtin_amdgcn_global_load_lds((const void*)(src[b] + sl * 64), LDS_PTR(dst + b * 512),
+                                       16, 0, kWeightPolicy);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          acc[s][t] =
-              mfma16(__builtin_nontemporal_load((const u32x4*)(wp[s] + ks * 32)), fx, acc[s][t]);
+    for (int b = WBLK; b < NDMA; ++b)
+      __builtin_amdgcn_global_load_lds((const void*)(src[b] + sl * 64), LDS_PTR(dst + b * 512),
+                                       16, 0, 0);
+  };
+  auto slot = [](int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); };
+  f32x4 acc[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) dma(s0 + i, ring[wave][i]);
+    for (int i = 0; i < n; ++i) {
+      // the stage refilled now was read in the previous iteration: its reads are done
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & kLgkm0);
+      asm volatile("" ::: "memory");
+      dma(s0 + i + D - 1, ring[wave][(i + D - 1) % D]);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * NDMA));  // slab i has landed
+      asm volatile("" ::: "memory");
+      const uint16_t* cur = ring[wave][i % D];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // two 32-k MFMA steps per slab
+        const int c = j * 4 + (lane >> 4);
+        const u32x4 fx = *(const u32x4*)(cur + WBLK * 512 + slot(lane & 15, c));
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const u32x4 fw = *(const u32x4*)(cur + slot(16 * q + (lane & 15), c));
+          acc[q] = mfma16(fw, fx, acc[q]);
+        }
       }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
   }
+  // partial sums go to the wave's own (drained) first stage
   if (wave > 0) {
+    f32x4* red = (f32x4*)ring[wave][0];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) red[wave - 1][s][t][lane] = acc[s][t];
+    for (int q = 0; q < NS; ++q) red[q * 64 + lane] = acc[q];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int q = 0; q < 3; ++q)
+  for (int w = 1; w < 4; ++w) {
+    const f32x4* red = (const f32x4*)ring[w][0];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[s][t] += red[q][s][t][lane];
-  // D[n = feature][m = row]: lane holds row (lane & 15) of each m-tile and
-  // features 4*(lane>>4) + 0..3.
+    for (int q = 0; q < NS; ++q) acc[q] += red[q * 64 + lane];
+  }
+  // D[n = feature][m = row]: lane holds row (lane & 15), features 4*(lane>>4)+0..3
   const int nn = tl.n0 + 4 * (lane >> 4);
-  if (nn >= N) return;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int row = tl.m0 + t * 16 + (lane & 15);
-    if (row >= tl.m_end) continue;
-    if (UPGATE) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(silu_mul(acc[1][t][0], acc[0][t][0])) |
-             ((uint32_t)f32_to_bf16(silu_mul(acc[1][t][1], acc[0][t][1])) << 16);
-      pk.y = (uint32_t)f32_to_bf16(silu_mul(acc[1][t][2], acc[0][t][2])) |
-             ((uint32_t)f32_to_bf16(silu_mul(acc[1][t][3], acc[0][t][3])) << 16);
-      *(uint2*)((uint16_t*)a.out + (int64_t)row * a.ldo + nn) = pk;
-    } else {
-      *(float4*)((float*)a.out + (int64_t)row * a.ldo + nn) =
-          make_float4(acc[0][t][0], acc[0][t][1], acc[0][t][2], acc[0][t][3]);
-    }
+  const int row = tl.m0 + (lane & 15);
+  if (nn >= N || row >= tl.m_end) return;
+  if (UPGATE) {
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(silu_mul(acc[1][0], acc[0][0])) |
+           ((uint32_t)f32_to_bf16(silu_mul(acc[1][1], acc[0][1])) << 16);
+    pk.y = (uint32_t)f32_to_bf16(silu_mul(acc[1][2], acc[0][2])) |
+           ((uint32_t)f32_to_bf16(silu_mul(acc[1][3], acc[0][3])) << 16);
+    *(uint2*)((uint16_t*)a.out + (int64_t)row * a.ldo + nn) = pk;
+  } else {
+    *(float4*)((float*)a.out + (int64_t)row * a.ldo + nn) =
+        make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
   }
 }
 
@@ -564,7 +574,7 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     return hipGetLastError();
   }
   if (P.kind == KIND_BF16_DECODE)
-    hipLaunchKernelGGL(gemm_bf16_stream_kernel<true>, grid, block, 0, s, up_args(P, x));
+    hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 128, 32, true>), grid, block, 0, s,
                        up_args(P, x));
@@ -587,7 +597,7 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     return hipGetLastError();
   }
   if (P.kind == KIND_BF16_DECODE)
-    hipLaunchKernelGGL(gemm_bf16_stream_kernel<false>, grid, block, 0, s, down_args(P, x));
+    hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 256, 128, 64, false>), grid, block, 0, s,
                        down_args(P, x));

@@ -13,13 +13,13 @@ static int prefill_rows(const moe_desc* d) {
   return d->T * d->k >= 384LL * d->E ? 256 : 128;
 }
 int up_row_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : 32;
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 int up_col_tile(int kind) {
   return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 int down_row_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : 32;
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 int down_col_tile(int kind) {
   return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_BF16_DECODE ? 16 : 32;
