@@ -14,9 +14,11 @@
 // token tile, so each lane ends with 4 consecutive output features of one
 // token, which it stores as one 8-byte (bf16 h) or 16-byte (fp32 out) write.
 // Both operands are K-contiguous in memory and staged through LDS in 64-wide
-// K slabs, double-buffered, with the 16-byte chunks of a row XOR-swizzled so
-// that the lanes of each ds_read_b128 phase hit distinct banks.  Fragments of
-// the next k-step are read from LDS while the current MFMAs run.
+// K slabs (one 128-byte line per tile row), copied by global_load_lds_dwordx4
+// in 1 KB bursts of 8 whole rows, into a ring of 2-3 stages, with the 16-byte
+// chunks of a row XOR-swizzled so that the lanes of each ds_read_b128 phase
+// hit distinct banks.  Fragments of the next k-step are read from LDS while
+// the current MFMAs run.
 // The up/gate tile holds the up and the gate rows of the same features, so
 // SwiGLU is applied in registers before h is written.
 //
@@ -46,13 +48,14 @@ struct GemmArgs {
   int64_t split_stride;       // elements between the outputs of consecutive K ranges
 };
 
-constexpr int BK = 32;  // K slab: 4 chunks of 8 bf16 per tile row (64 bytes)
+constexpr int BK = 64;  // K slab: 8 chunks of 8 bf16 per tile row (one 128-byte line)
 
-// LDS element offset of 16-byte chunk `chunk` of tile row `row`.  A
-// ds_read_b128 phase serves 16 lanes that read one chunk of 16 consecutive
-// rows; XOR-ing the chunk with (row / 4) % 4 spreads them over all 64 banks.
+// LDS element offset of 16-byte chunk `chunk` of tile row `row` (rows of 128
+// bytes).  A ds_read_b128 phase serves 16 lanes that read one chunk of 16
+// consecutive rows; XOR-ing the chunk with (row / 2) % 8 spreads them over
+// all 64 banks.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3);
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 // A tile entry read by every lane, made wave-uniform (scalar registers).
@@ -83,30 +86,32 @@ __device__ __forceinline__ int tile_of_block(const Tile* tiles, int remap = 1) {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kLgkm0 = ~(15 << 8);  // AND into an immediate to also wait lgkmcnt(0)
 
-// One stage of a tile operand: 1 KB blocks of 16 rows, block b = wave + 4 i.
+// One stage of a tile operand: 1 KB blocks of 8 rows, block b = wave + 4 i.
 // global_load_lds_dwordx4 fills bytes [16 l, 16 l + 16) of a block from lane
-// l, so lane l fetches row 16 b + l / 4 at the chunk whose swizzled slot is
-// l % 4.
-template <int NBLK>
+// l, so lane l fetches row 8 b + l / 8 at the chunk whose swizzled slot is
+// l % 8: the 8 lanes of a row read its whole 128-byte line.
+template <int NBLK, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const char* base, const uint32_t* off, uint16_t* lds,
                                          int wave) {
 #pragma unroll
   for (int i = 0; i < NBLK; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                     LDS_PTR(lds + (wave + 4 * i) * 512), 16, 0, 0);
+                                     LDS_PTR(lds + (wave + 4 * i) * 512), 16, 0, AUX);
 }
 
-template <int BM, int BN, int WM, int WN, bool UPGATE>
+constexpr int kPolW = 0, kPolX = 0;  // cache policy bits of the weight / token bursts
+template <int BM, int BN, int WM, int WN, bool UPGATE, int NST>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WROWS = UPGATE ? 2 * BN : BN;        // weight rows in the tile
   constexpr int NWN = BN / WN, NWM = BM / WM;
   static_assert(NWN * NWM == 4, "4 waves");
   constexpr int TN = WN / 32, TM = WM / 32;           // 32x32 sub-tiles per wave
   constexpr int NS = UPGATE ? 2 : 1;                  // up and gate, or down
-  constexpr int WB = WROWS / 64;                      // 1 KB blocks per wave and stage
-  constexpr int XB = BM / 64;
+  constexpr int WB = WROWS / 32;                      // 1 KB blocks per wave and stage
+  constexpr int XB = BM / 32;
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
+  static_assert(NST == 2 || NST == 3, "stages");
 
   // With a K split, workgroup slots [q*count, (q+1)*count) run K range q of
   // every tile and write their partial sums to output q.
@@ -131,50 +136,45 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const uint16_t* W1 = UPGATE ? (sh ? a.s1 + (tl.g - a.E) * wstride : a.w1 + tl.g * wstride)
                               : nullptr;
 
-  // Four stage buffers per operand, as separate arrays so the compiler can
-  // tell reads of one buffer from DMA still landing in another.
-  __shared__ __attribute__((aligned(1024))) uint16_t lw0[WROWS * BK], lw1[WROWS * BK],
-      lw2[WROWS * BK], lw3[WROWS * BK];
-  __shared__ __attribute__((aligned(1024))) uint16_t lx0[BM * BK], lx1[BM * BK], lx2[BM * BK],
-      lx3[BM * BK];
+  // NST stage buffers per operand, as separate arrays so the compiler can
+  // tell reads of one buffer from DMA still landing in another (an unused
+  // third one is a token 16 bytes).
+  constexpr int SW = WROWS * BK, SX = BM * BK;
+  __shared__ __attribute__((aligned(1024))) uint16_t lw0[SW], lw1[SW], lw2[NST > 2 ? SW : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lx0[SX], lx1[SX], lx2[NST > 2 ? SX : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Source byte offsets: block b = wave + 4 i holds tile rows 16 b .. 16 b + 15;
-  // lane l reads row 16 b + l / 4 at chunk (l % 4) ^ ((row / 4) % 4), and
-  // (row / 4) % 4 = (l / 16) % 4.
-  const int rr = lane >> 2;
-  const int gch = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t woff[WB];
+  // Source byte offsets: block b = wave + 4 i holds tile rows 8 b .. 8 b + 7;
+  // lane l reads row 8 b + l / 8 at chunk (l % 8) ^ ((row / 2) % 8), where
+  // (row / 2) % 8 = 4 (wave % 2) + (l / 16) does not depend on i.  The gate
+  // rows of an up/gate tile sit BN rows below the up rows of the same
+  // features, so both halves share the offsets.
+  const int rr = lane >> 3;
+  const int gch = (lane & 7) ^ (((wave & 1) << 2) + (lane >> 4));
+  constexpr int WOFF = UPGATE ? WB / 2 : WB;
+  uint32_t woff[WOFF];
 #pragma unroll
-  for (int i = 0; i < WB; ++i) {
-    const int r = 16 * (wave + 4 * i) + rr;
-    int n = tl.n0 + (UPGATE && r >= BN ? r - BN : r);
+  for (int i = 0; i < WOFF; ++i) {
+    int n = tl.n0 + 8 * (wave + 4 * i) + rr;
     n = n < N ? n : N - 1;
     woff[i] = ((uint32_t)n * (uint32_t)K + gch * 8) * 2;
   }
   uint32_t xoff[XB];
 #pragma unroll
   for (int i = 0; i < XB; ++i) {
-    int row = tl.m0 + 16 * (wave + 4 * i) + rr;
+    int row = tl.m0 + 8 * (wave + 4 * i) + rr;
     row = row < tl.m_end ? row : tl.m_end - 1;
     const uint32_t src_row = a.sorted ? (uint32_t)a.sorted[row] : (uint32_t)row;
     xoff[i] = (src_row * (uint32_t)a.ldt + gch * 8) * 2;
   }
-  // With WB blocks per wave, the first WB/2 hold up rows (tile rows < BN).
   const int nk_all = K / BK;
   const int kb = split * nk_all / a.ksplit;  // first slab of this K range
   auto dma = [&](int kt_local, uint16_t* lw, uint16_t* lx) {
     const int kt = kb + kt_local;
-    const char* bw0 = (const char*)(W0 + kt * BK);
-    if (UPGATE) {
-      dma_tile<WB / 2>(bw0, woff, lw, wave);
-      dma_tile<WB / 2>((const char*)(W1 + kt * BK), woff + WB / 2, lw + 4 * (WB / 2) * 512,
-                       wave);
-    } else {
-      dma_tile<WB>(bw0, woff, lw, wave);
-    }
-    dma_tile<XB>((const char*)(a.tok + kt * BK), xoff, lx, wave);
+    dma_tile<WOFF, kPolW>((const char*)(W0 + kt * BK), woff, lw, wave);
+    if (UPGATE) dma_tile<WOFF, kPolW>((const char*)(W1 + kt * BK), woff, lw + BN * BK, wave);
+    dma_tile<XB, kPolX>((const char*)(a.tok + kt * BK), xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -188,24 +188,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][i][j][r] = 0.f;
 
-  // Fragment read offsets (elements) of the two k-steps of a slab: row of
-  // sub-tile 0; the other sub-tiles are whole 32-row blocks further.
-  int fxo[2], fwo[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
-    fxo[kk] = swz(wm * WM + (lane & 31), ch);
-    fwo[kk] = swz(wn * WN + (lane & 31), ch);
-  }
-  u32x4 fx0[TM], fw0[NS][TN], fx1[TM], fw1[NS][TN];  // fragments of k-step 0 / 1
+  // Fragment read offsets (elements) of k-step 0 of a slab: lane l reads row
+  // (l % 32) of sub-tile 0 at chunk l / 32; the other sub-tiles are whole
+  // 32-row blocks further.  Chunk 2 kk + c of a row sits at the slot of chunk
+  // c XOR 2 kk, so k-step kk is k-step 0's offset XOR 16 kk.
+  const int fxo = swz(wm * WM + (lane & 31), lane >> 5);
+  const int fwo = swz(wn * WN + (lane & 31), lane >> 5);
+  u32x4 fxA[TM], fwA[NS][TN], fxB[TM], fwB[NS][TN];  // fragments of even / odd k-steps
   auto fload = [&](const uint16_t* lw, const uint16_t* lx, int kk, u32x4* fx, u32x4 (*fw)[TN]) {
+    const int ox = fxo ^ (kk << 4), ow = fwo ^ (kk << 4);
 #pragma unroll
-    for (int j = 0; j < TM; ++j) fx[j] = *(const u32x4*)(&lx[fxo[kk] + j * 32 * BK]);
+    for (int j = 0; j < TM; ++j) fx[j] = *(const u32x4*)(&lx[ox + j * 32 * BK]);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
-        fw[s][i] = *(const u32x4*)(&lw[fwo[kk] + (s * BN + i * 32) * BK]);
+        fw[s][i] = *(const u32x4*)(&lw[ow + (s * BN + i * 32) * BK]);
   };
   auto mfmas = [&](const u32x4* fx, u32x4 (*fw)[TN]) {
 #pragma unroll
@@ -217,19 +215,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   };
   constexpr int NF = TM + NS * TN;   // fragment reads per k-step
   constexpr int NMF = NS * TN * TM;  // MFMAs per k-step
-  static_assert(NMF >= NF, "pipeline shape");
-  // Issue order for one k-step: one MFMA, then one fragment read (and one DMA
-  // when `dmas`), NF times; the remaining MFMAs last.
-  auto pipeline = [&](bool dmas) {
+  constexpr int ND0 = (NDMA + 1) / 2, ND1 = NDMA - ND0;  // DMAs issued in k-steps 0 and 1
+  static_assert(NMF >= NF && NMF >= ND0, "pipeline shape");
+  // Issue order for one k-step: MFMAs one by one, each followed by one
+  // fragment read (the first NF) and one DMA (the first nd).
+  auto pipeline = [&](int nd) {
 #pragma unroll
-    for (int r = 0; r < NF; ++r) {
+    for (int r = 0; r < NMF; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (dmas && r < NDMA) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (r < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r < nd) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
-    if (dmas)
-      for (int r = NF; r < NDMA; ++r) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NF, 0);
   };
   auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -242,9 +238,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   // fragment read is done), then for all waves.
   auto wait_slabs = [&](int n) {
     __builtin_amdgcn_sched_barrier(0);
-    if (n >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA) & kLgkm0);
-    else if (n == 1)
+    if (n > 0)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA) & kLgkm0);
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & kLgkm0);
@@ -252,47 +246,60 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   };
 
   const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
-  // The first nk % 4 slabs go through buffer 0 one at a time, so the ring
-  // below always runs a whole number of 4-slab turns.
-  const int r0 = nk & 3;
+  // The first nk % NST slabs go through buffer 0 one at a time, so the ring
+  // below always runs a whole number of NST-slab turns.
+  const int r0 = nk % NST;
   for (int kt = 0; kt < r0; ++kt) {
     dma(kt, lw0, lx0);
     wait_slabs(0);
-    fload(lw0, lx0, 0, fx0, fw0);
-    fload(lw0, lx0, 1, fx1, fw1);
-    mfmas(fx0, fw0);
-    mfmas(fx1, fw1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      fload(lw0, lx0, kk, fxA, fwA);
+      mfmas(fxA, fwA);
+    }
     wait_slabs(0);
   }
   const int m = nk - r0;
   if (m > 0) {
     dma(r0 + 0, lw0, lx0);
-    dma(r0 + 1, lw1, lx1);
-    dma(r0 + 2, lw2, lx2);
-    wait_slabs(2);
-    fload(lw0, lx0, 0, fx0, fw0);
-    // One slab: DMA the slab three ahead into the buffer freed last slab;
-    // k-step 0 MFMAs while reading k-step 1 fragments; wait until the next
-    // slab has landed; k-step 1 MFMAs while reading the next slab's k-step 0.
-    // No branches, so each half is one scheduling region: near the end the
-    // DMA re-fetches the last slab into a buffer nothing reads any more, and
-    // the final next-slab read is simply unused.
-#define MOE_SLAB(J, LWC, LXC, LWN, LXN, LWT, LXT) \
-    {                                             \
-      dma(r0 + min((J) + 3, m - 1), LWT, LXT);    \
-      fload(LWC, LXC, 1, fx1, fw1);               \
-      mfmas(fx0, fw0);                            \
-      pipeline(true);                             \
-      wait_slabs(2);                              \
-      fload(LWN, LXN, 0, fx0, fw0);               \
-      mfmas(fx1, fw1);                            \
-      pipeline(false);                            \
+    if (NST > 2) dma(r0 + 1, lw1, lx1);
+    wait_slabs(NST - 2);
+    fload(lw0, lx0, 0, fxA, fwA);
+    // One slab of four k-steps: DMA the slab NST - 1 ahead into the buffer
+    // freed last slab; each k-step's MFMAs run while the next k-step's
+    // fragments are read; before the last k-step's MFMAs, wait until the
+    // next slab has landed and read its first fragments.  No branches, so
+    // each stretch between barriers is one scheduling region: near the end
+    // the DMA re-fetches the last slab into a buffer nothing reads any more,
+    // and the final next-slab read is simply unused.
+#define MOE_SLAB(J, LWC, LXC, LWN, LXN, LWT, LXT)    \
+    {                                                \
+      dma(r0 + min((J) + NST - 1, m - 1), LWT, LXT); \
+      fload(LWC, LXC, 1, fxB, fwB);                  \
+      mfmas(fxA, fwA);                               \
+      pipeline(ND0);                                 \
+      fload(LWC, LXC, 2, fxA, fwA);                  \
+      mfmas(fxB, fwB);                               \
+      pipeline(ND1);                                 \
+      fload(LWC, LXC, 3, fxB, fwB);                  \
+      mfmas(fxA, fwA);                               \
+      pipeline(0);                                   \
+      wait_slabs(NST - 2);                           \
+      fload(LWN, LXN, 0, fxA, fwA);                  \
+      mfmas(fxB, fwB);                               \
+      pipeline(0);                                   \
     }
-    for (int j = 0; j < m; j += 4) {
-      MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw3, lx3)
-      MOE_SLAB(j + 1, lw1, lx1, lw2, lx2, lw0, lx0)
-      MOE_SLAB(j + 2, lw2, lx2, lw3, lx3, lw1, lx1)
-      MOE_SLAB(j + 3, lw3, lx3, lw0, lx0, lw2, lx2)
+    if constexpr (NST == 2) {
+      for (int j = 0; j < m; j += 2) {
+        MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw1, lx1)
+        MOE_SLAB(j + 1, lw1, lx1, lw0, lx0, lw0, lx0)
+      }
+    } else {
+      for (int j = 0; j < m; j += 3) {
+        MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw2, lx2)
+        MOE_SLAB(j + 1, lw1, lx1, lw2, lx2, lw0, lx0)
+        MOE_SLAB(j + 2, lw2, lx2, lw0, lx0, lw1, lx1)
+      }
     }
 #undef MOE_SLAB
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
@@ -561,6 +568,10 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
                   (int64_t)((size_t)P.R + kRowSlack) * D.d};
 }
 
+// LDS stages of each prefill GEMM instantiation (at most 160 KB of LDS:
+// 64 KB per stage for 256x256-row tiles, 48 KB for 128-row tiles).
+constexpr int kStagesUp128 = 3, kStagesUp256 = 2, kStagesDown128 = 3, kStagesDown256 = 2;
+
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   const moe_desc& D = P.desc;
   const dim3 block(256);
@@ -576,10 +587,10 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 128, 32, true>), grid, block, 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 128, 32, true, kStagesUp128>), grid, block, 0, s,
                        up_args(P, x));
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 128, 64, true>), grid, block, 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 128, 64, true, kStagesUp256>), grid, block, 0, s,
                        up_args(P, x));
   return hipGetLastError();
 }
@@ -599,10 +610,10 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 256, 128, 64, false>), grid, block, 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 256, 128, 64, false, kStagesDown128>), grid, block, 0, s,
                        down_args(P, x));
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 128, 128, false>), grid, block, 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 128, 128, false, kStagesDown256>), grid, block, 0, s,
                        down_args(P, x));
   return hipGetLastError();
 }

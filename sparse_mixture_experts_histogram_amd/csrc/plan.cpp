@@ -15,13 +15,13 @@ static int prefill_rows(const moe_desc* d) {
 int up_row_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
 }
-int up_col_tile(int kind) {
+int up_col_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 int down_row_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
 }
-int down_col_tile(int kind) {
+int down_col_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_BF16_DECODE ? 16 : 32;
 }
 
@@ -79,8 +79,8 @@ int make_plan(const moe_desc* d, Plan* p) {
     s.max_tiles = s.max_row_tiles * s.n_tiles;
     return s;
   };
-  P.up = shape(up_row_tile(P.kind, d), up_col_tile(P.kind), d->ffn, d->ffn_shared);
-  P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind), d->d, d->d);
+  P.up = shape(up_row_tile(P.kind, d), up_col_tile(P.kind, d), d->ffn, d->ffn_shared);
+  P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind, d), d->d, d->d);
   // the decode kernels walk a compact list of row tiles (see dispatch.hip)
   P.up.row_list = P.down.row_list = P.kind == KIND_BF16_DECODE;
   // Schedule order (measured on MI355X): the up/gate GEMM runs chunks of

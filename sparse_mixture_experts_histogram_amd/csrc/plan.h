@@ -62,8 +62,8 @@ int make_plan(const moe_desc* d, Plan* p);
 
 // Tile shapes of the grouped GEMMs per kernel family.
 int up_row_tile(int kind, const moe_desc* d);
-int up_col_tile(int kind);
+int up_col_tile(int kind, const moe_desc* d);
 int down_row_tile(int kind, const moe_desc* d);
-int down_col_tile(int kind);
+int down_col_tile(int kind, const moe_desc* d);
 
 }  // namespace moe
