@@ -108,8 +108,9 @@ def time_forward(x, W, k, steps, warmup):
 
 
 def time_decode(x, W, k, iters):
-    """Per-iteration event timing with the 256 MB MALL flushed (a 1 GiB write)
-    between iterations, outside the timed interval; median."""
+    """Per-iteration event timing with L2 and the 256 MB MALL flushed between
+    iterations, outside the timed interval, by reading 1 GiB (a read leaves no
+    dirty lines for the next kernel to write back); median."""
     import torch
     import sparse_mixture_experts_histogram_amd as moe
     from sparse_mixture_experts_histogram_amd.hipevents import Events
@@ -118,12 +119,13 @@ def time_decode(x, W, k, iters):
     ws = moe.workspace(W.desc(T, k), x.device)
     y = torch.empty((T, x.shape[1]), dtype=torch.float32, device=x.device)
     counts = torch.empty((W.w_up.shape[0],), dtype=torch.int32, device=x.device)
-    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=x.device)
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=x.device)
+    flush_sum = torch.empty((), dtype=torch.float32, device=x.device)
     ev = Events(6 * iters)
     for _ in range(5):
         moe.moe_forward_timed(x, W, k, None, y, ws, counts=counts)
     for i in range(iters):
-        flush.zero_()
+        torch.sum(flush, dim=0, out=flush_sum)
         moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
     torch.cuda.synchronize()
     layer = statistics.median(ev.ms(6 * i, 6 * i + 5) for i in range(iters))

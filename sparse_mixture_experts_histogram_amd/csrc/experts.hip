@@ -86,29 +86,31 @@ __device__ __forceinline__ int tile_of_block(const Tile* tiles, int remap = 1) {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kLgkm0 = ~(15 << 8);  // AND into an immediate to also wait lgkmcnt(0)
 
-// One stage of a tile operand: 1 KB blocks of 8 rows, block b = wave + 4 i.
+// One stage of a tile operand: 1 KB blocks of 8 rows, block b = wave + NW i.
 // global_load_lds_dwordx4 fills bytes [16 l, 16 l + 16) of a block from lane
 // l, so lane l fetches row 8 b + l / 8 at the chunk whose swizzled slot is
 // l % 8: the 8 lanes of a row read its whole 128-byte line.
-template <int NBLK, int AUX = 0>
+template <int NBLK, int NW, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const char* base, const uint32_t* off, uint16_t* lds,
                                          int wave) {
 #pragma unroll
   for (int i = 0; i < NBLK; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                     LDS_PTR(lds + (wave + 4 * i) * 512), 16, 0, AUX);
+                                     LDS_PTR(lds + (wave + NW * i) * 512), 16, 0, AUX);
 }
 
 constexpr int kPolW = 0, kPolX = 0;  // cache policy bits of the weight / token bursts
+constexpr int kSpread = 2;            // k-steps of a slab over which its DMAs are issued
 template <int BM, int BN, int WM, int WN, bool UPGATE, int NST>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WROWS = UPGATE ? 2 * BN : BN;        // weight rows in the tile
   constexpr int NWN = BN / WN, NWM = BM / WM;
-  static_assert(NWN * NWM == 4, "4 waves");
+  constexpr int NW = NWN * NWM;                       // waves
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int TN = WN / 32, TM = WM / 32;           // 32x32 sub-tiles per wave
   constexpr int NS = UPGATE ? 2 : 1;                  // up and gate, or down
-  constexpr int WB = WROWS / 32;                      // 1 KB blocks per wave and stage
-  constexpr int XB = BM / 32;
+  constexpr int WB = WROWS / (8 * NW);                // 1 KB blocks per wave and stage
+  constexpr int XB = BM / (8 * NW);
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
   static_assert(NST == 2 || NST == 3, "stages");
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Source byte offsets: block b = wave + 4 i holds tile rows 8 b .. 8 b + 7;
+  // Source byte offsets: block b = wave + NW i holds tile rows 8 b .. 8 b + 7;
   // lane l reads row 8 b + l / 8 at chunk (l % 8) ^ ((row / 2) % 8), where
   // (row / 2) % 8 = 4 (wave % 2) + (l / 16) does not depend on i.  The gate
   // rows of an up/gate tile sit BN rows below the up rows of the same
@@ -156,14 +158,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   uint32_t woff[WOFF];
 #pragma unroll
   for (int i = 0; i < WOFF; ++i) {
-    int n = tl.n0 + 8 * (wave + 4 * i) + rr;
+    int n = tl.n0 + 8 * (wave + NW * i) + rr;
     n = n < N ? n : N - 1;
     woff[i] = ((uint32_t)n * (uint32_t)K + gch * 8) * 2;
   }
   uint32_t xoff[XB];
 #pragma unroll
   for (int i = 0; i < XB; ++i) {
-    int row = tl.m0 + 8 * (wave + 4 * i) + rr;
+    int row = tl.m0 + 8 * (wave + NW * i) + rr;
     row = row < tl.m_end ? row : tl.m_end - 1;
     const uint32_t src_row = a.sorted ? (uint32_t)a.sorted[row] : (uint32_t)row;
     xoff[i] = (src_row * (uint32_t)a.ldt + gch * 8) * 2;
@@ -172,9 +174,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int kb = split * nk_all / a.ksplit;  // first slab of this K range
   auto dma = [&](int kt_local, uint16_t* lw, uint16_t* lx) {
     const int kt = kb + kt_local;
-    dma_tile<WOFF, kPolW>((const char*)(W0 + kt * BK), woff, lw, wave);
-    if (UPGATE) dma_tile<WOFF, kPolW>((const char*)(W1 + kt * BK), woff, lw + BN * BK, wave);
-    dma_tile<XB, kPolX>((const char*)(a.tok + kt * BK), xoff, lx, wave);
+    dma_tile<WOFF, NW, kPolW>((const char*)(W0 + kt * BK), woff, lw, wave);
+    if (UPGATE)
+      dma_tile<WOFF, NW, kPolW>((const char*)(W1 + kt * BK), woff, lw + BN * BK, wave);
+    dma_tile<XB, NW, kPolX>((const char*)(a.tok + kt * BK), xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -215,8 +218,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   };
   constexpr int NF = TM + NS * TN;   // fragment reads per k-step
   constexpr int NMF = NS * TN * TM;  // MFMAs per k-step
-  constexpr int ND0 = (NDMA + 1) / 2, ND1 = NDMA - ND0;  // DMAs issued in k-steps 0 and 1
-  static_assert(NMF >= NF && NMF >= ND0, "pipeline shape");
+  // DMAs issued during k-steps 0, 1 and 2 of a slab
+  constexpr int ND0 = (NDMA + kSpread - 1) / kSpread;
+  constexpr int ND1 = kSpread >= 2 ? (NDMA - ND0 + kSpread - 2) / (kSpread - 1) : 0;
+  constexpr int ND2 = NDMA - ND0 - ND1;
+  static_assert(NMF >= NF && NMF >= ND0 && NMF >= ND1 && NMF >= ND2, "pipeline shape");
   // Issue order for one k-step: MFMAs one by one, each followed by one
   // fragment read (the first NF) and one DMA (the first nd).
   auto pipeline = [&](int nd) {
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
       pipeline(ND1);                                 \
       fload(LWC, LXC, 3, fxB, fwB);                  \
       mfmas(fxA, fwA);                               \
-      pipeline(0);                                   \
+      pipeline(ND2);                                 \
       wait_slabs(NST - 2);                           \
       fload(LWN, LXN, 0, fxA, fwA);                  \
       mfmas(fxB, fwB);                               \
@@ -571,6 +577,16 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
 // LDS stages of each prefill GEMM instantiation (at most 160 KB of LDS:
 // 64 KB per stage for 256x256-row tiles, 48 KB for 128-row tiles).
 constexpr int kStagesUp128 = 3, kStagesUp256 = 2, kStagesDown128 = 3, kStagesDown256 = 2;
+// Per-wave tile (rows x output columns) of the 256-row instantiations; the
+// wave count is (BM / WM) * (BN / WN).
+constexpr int kUp256WM = 128, kUp256WN = 64, kDown256WM = 128, kDown256WN = 128;
+
+template <int BM, int BN, int WM, int WN, bool UPGATE, int NST>
+static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
+  constexpr int nw = (BM / WM) * (BN / WN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NST>), grid, dim3(64 * nw), 0, s,
+                     a);
+}
 
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   const moe_desc& D = P.desc;
@@ -587,11 +603,9 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 128, 32, true, kStagesUp128>), grid, block, 0, s,
-                       up_args(P, x));
+    launch_gemm<128, 128, 128, 32, true, kStagesUp128>(grid, s, up_args(P, x));
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 128, 64, true, kStagesUp256>), grid, block, 0, s,
-                       up_args(P, x));
+    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kStagesUp256>(grid, s, up_args(P, x));
   return hipGetLastError();
 }
 
@@ -610,11 +624,9 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 256, 128, 64, false, kStagesDown128>), grid, block, 0, s,
-                       down_args(P, x));
+    launch_gemm<128, 256, 128, 64, false, kStagesDown128>(grid, s, down_args(P, x));
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 128, 128, false, kStagesDown256>), grid, block, 0, s,
-                       down_args(P, x));
+    launch_gemm<256, 256, kDown256WM, kDown256WN, false, kStagesDown256>(grid, s, down_args(P, x));
   return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@ template <int EPL>
 __device__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int t0, int T,
                            int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                            int32_t* sel) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int tl = wave; tl < kRouterTokens; tl += 4) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  for (int tl = wave; tl < kRouterTokens; tl += nwaves) {
     const int t = t0 + tl;
     if (t >= T) break;
     uint64_t key[EPL];
@@ -111,20 +111,17 @@ __device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const floa
     router_tail<8>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
 }
 
-// Dynamic LDS: KS partial logit tiles [KS][16][ld] floats, then sel[16*k].
-template <int NT>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int k, int KS, int32_t* idx_out,
-    float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
-  extern __shared__ float lds[];
+// Logits of the kRouterTokens tokens from t0 over k-steps [kb0, kb1) (32 k
+// each) for every expert, into lg[16][ld] (LDS, which must hold KS partial
+// tiles [KS][16][ld]).  NW waves: wave w sums K part w % KS of the expert
+// tiles w / KS + i NW / KS; the KS partial tiles are then added in order.
+template <int NT, int NW>
+__device__ void block_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                             int T, int d, int E, int KS, int t0, int kb0, int kb1, float* lg,
+                             int ld) {
   const int etiles = (E + 15) >> 4;
-  const int ld = etiles * 16 + 4;
-  float* lg = lds;
-  int32_t* sel = (int32_t*)(lds + KS * kRouterTokens * ld);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t0 = blockIdx.x * kRouterTokens;
-  const int ks = wave % KS, tg = wave / KS, tstep = 4 / KS;
+  const int ks = wave % KS, tg = wave / KS, tstep = NW / KS;
 
   int row = t0 + (lane & 15);
   row = row < T ? row : T - 1;
@@ -140,30 +137,28 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   }
   // K loop in batches of U k-steps: all loads of a batch are issued before
   // its MFMAs, so each wave keeps U*(NT+1) 16-byte loads per lane in flight.
+  // The last batch re-reads the last k-step for its slots past the range and
+  // zeroes their token fragment, so every batch is one round of loads.
   // Tiles past the last expert read a clamped row and are not stored.
-  constexpr int U = 4;
-  const int nk = d >> 5;
-  const int c0 = ks * nk / KS, c1 = (ks + 1) * nk / KS;
-  int c = c0;
-  for (; c + U <= c1; c += U) {
+  constexpr int U = NT <= 2 ? 8 : 4;
+  const int c0 = kb0 + ks * (kb1 - kb0) / KS, c1 = kb0 + (ks + 1) * (kb1 - kb0) / KS;
+  for (int c = c0; c < c1; c += U) {
     u32x4 a[U], b[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      a[u] = *(const u32x4*)(xp + (c + u) * 32);
+      const int cu = min(c + u, c1 - 1);
+      a[u] = *(const u32x4*)(xp + cu * 32);
 #pragma unroll
-      for (int i = 0; i < NT; ++i) b[u][i] = *(const u32x4*)(wp[i] + (c + u) * 32);
+      for (int i = 0; i < NT; ++i) b[u][i] = *(const u32x4*)(wp[i] + cu * 32);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (c + u >= c1) a[u] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < NT; ++i) acc[i] = mfma16(a[u], b[u][i], acc[i]);
+    }
     __builtin_amdgcn_sched_group_barrier(0x020, U * (NT + 1), 0);  // every load first
     __builtin_amdgcn_sched_group_barrier(0x008, U * NT, 0);        // then the MFMAs
-  }
-  for (; c < c1; ++c) {
-    const u32x4 a = *(const u32x4*)(xp + c * 32);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = mfma16(a, *(const u32x4*)(wp[i] + c * 32), acc[i]);
   }
   // D[m = token][n = expert]: lane holds expert (lane & 15), tokens 4*(lane>>4)+r
 #pragma unroll
@@ -184,7 +179,21 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
     __syncthreads();
   }
-  router_tail_dispatch(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+}
+
+// One token block per workgroup, whole K.  Dynamic LDS: KS partial logit
+// tiles [KS][16][ld] floats, then sel[16*k].
+template <int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k, int KS, int32_t* idx_out,
+    float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
+  extern __shared__ float lds[];
+  const int ld = ((E + 15) >> 4) * 16 + 4;
+  int32_t* sel = (int32_t*)(lds + KS * kRouterTokens * ld);
+  const int t0 = blockIdx.x * kRouterTokens;
+  block_logits<NT, NW>(x, wr, T, d, E, KS, t0, 0, d >> 5, lds, ld);
+  router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -232,34 +241,40 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
                          hipStream_t s) {
   const moe_desc& D = P.desc;
-  const dim3 grid((unsigned)P.nblk), block(256);
+  const dim3 grid((unsigned)P.nblk);
   const size_t sel_bytes = (size_t)kRouterTokens * D.k * 4;
   if (D.dtype == MOE_F32) {
     const size_t lds = (size_t)kRouterTokens * (D.E + 1) * 4 + sel_bytes;
-    hipLaunchKernelGGL(router_f32_kernel, grid, block, lds, s, (const float*)x,
+    hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), lds, s, (const float*)x,
                        (const float*)w_router, bias, (int)D.T, D.d, D.E, D.k, idx, w, blk_hist,
                        blk_rank);
     return hipGetLastError();
   }
-  // Split K over the 4 waves as far as the per-wave tile count allows (at
-  // most 8 tiles of 16 experts per wave): small token counts then still have
-  // all four waves streaming the router matrix.
+  // 4 waves; K is split over as many of them as the expert tiles leave free
+  // (KS = 4 / tiles, a power of two), so even one token block keeps all four
+  // streaming the router matrix.  (Measured on MI355X: sixteen waves, or
+  // splitting one block's K range over several workgroups, were slower.)
+  constexpr int NW = 4;
   const int etiles = (D.E + 15) / 16;
-  const int KS = etiles <= 8 ? 4 : etiles <= 16 ? 2 : 1;
-  const int nt = (etiles + (4 / KS) - 1) / (4 / KS);
-  const size_t lds = (size_t)KS * kRouterTokens * (etiles * 16 + 4) * 4 + sel_bytes;
+  int KS = NW;
+  while (KS > 1 && KS * etiles > NW) KS >>= 1;
+  const int nt = (etiles + (NW / KS) - 1) / (NW / KS);
+  const int ld = etiles * 16 + 4;
+  const size_t lds = (size_t)KS * kRouterTokens * ld * 4 + sel_bytes;
+  const uint16_t* xb = (const uint16_t*)x;
+  const uint16_t* wb = (const uint16_t*)w_router;
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, lds, s, (const uint16_t*)x, (const uint16_t*)w_router,
-                       bias, (int)D.T, D.d, D.E, D.k, KS, idx, w, blk_hist, blk_rank);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, s, xb, wb, bias, (int)D.T, D.d, D.E, D.k,
+                       KS, idx, w, blk_hist, blk_rank);
   };
   if (nt <= 1)
-    args(router_bf16_kernel<1>);
+    args(router_bf16_kernel<1, NW>);
   else if (nt <= 2)
-    args(router_bf16_kernel<2>);
+    args(router_bf16_kernel<2, NW>);
   else if (nt <= 4)
-    args(router_bf16_kernel<4>);
+    args(router_bf16_kernel<4, NW>);
   else
-    args(router_bf16_kernel<8>);
+    args(router_bf16_kernel<8, NW>);
   return hipGetLastError();
 }
 
