@@ -68,14 +68,17 @@ __device__ __forceinline__ Tile uniform_tile(const Tile& t) {
 // one XCD (the dispatcher deals workgroup i to XCD i % 8), so the workgroups
 // that share weight and token tiles share that XCD's L2; without it, entries
 // are spread over all XCDs.
-__device__ __forceinline__ int tile_of_block(const Tile* tiles, int remap = 1) {
-  const int count = tiles[0].g;
+__device__ __forceinline__ int entry_of_block(int count, int remap) {
   const int bid = blockIdx.x;
   if (!remap) return bid < count ? bid : -1;
   const int per = (count + 7) >> 3;
   if (bid >= per * 8) return -1;
   const int L = (bid & 7) * per + (bid >> 3);
   return L < count ? L : -1;
+}
+
+__device__ __forceinline__ int tile_of_block(const Tile* tiles, int remap = 1) {
+  return entry_of_block(tiles[0].g, remap);
 }
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -115,19 +118,12 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
   static_assert(NST == 2 || NST == 3, "stages");
 
-  // With a K split, workgroup slots [q*count, (q+1)*count) run K range q of
-  // every tile and write their partial sums to output q.
-  int L, split = 0;
-  if (a.ksplit > 1) {
-    const int count = a.tiles[0].g;
-    const int bid = blockIdx.x;
-    if (bid >= count * a.ksplit) return;
-    split = bid / count;
-    L = bid - split * count;
-  } else {
-    L = tile_of_block(a.tiles, a.xcd_remap);
-    if (L < 0) return;
-  }
+  // With a K split, entries [q*count, (q+1)*count) run K range q of every
+  // tile and write their partial sums to output q.
+  const int count = a.tiles[0].g;
+  const int idx = entry_of_block(count * a.ksplit, a.xcd_remap);
+  if (idx < 0) return;
+  const int split = idx / count, L = idx - split * count;
   const Tile tl = uniform_tile(a.tiles[1 + L]);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
@@ -312,17 +308,27 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   }
 
   // D[n = feature][m = row]: lane holds row (lane & 31) and, for q = 0..3,
-  // features 8q + 4*(lane>>5) + 0..3 of each 32x32 sub-tile.
+  // features 8q + 4*(lane>>5) + 0..3 of each 32x32 sub-tile.  Outputs are
+  // written through LDS so that every store is a 16-byte piece of a whole
+  // row: each wave stages 32 rows x WN features of its tile at a time in a
+  // stage buffer of its own (row pitch padded by 16 bytes against bank
+  // conflicts), then 64 / (row bytes / 16) rows per store instruction.
+  constexpr int ES = UPGATE ? 2 : 4;                  // output element bytes
+  constexpr int RB = WN * ES, PITCH = RB + 16;        // staged row bytes, LDS pitch
+  constexpr int LPR = RB / 16, RPI = 64 / LPR;        // lanes per row, rows per store
+  static_assert(NW == 4 && RB % 16 == 0 && 64 % LPR == 0, "epilogue shape");
+  static_assert(32 * PITCH <= 2 * (SX < SW ? SX : SW), "staging fits a stage buffer");
+  __syncthreads();  // every wave is done reading the stage buffers
+  char* st = (char*)(wave == 0 ? lw0 : wave == 1 ? lw1 : wave == 2 ? lx0 : lx1);
+  const int row0 = tl.m0 + wm * WM, col0 = tl.n0 + wn * WN;
+  char* outb = (char*)a.out + (int64_t)split * a.split_stride * ES;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int row = tl.m0 + wm * WM + j * 32 + (lane & 31);
-    if (row >= tl.m_end) continue;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = tl.n0 + wn * WN + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (n >= N) continue;
+        char* dst = st + (lane & 31) * PITCH + (i * 32 + 8 * q + 4 * (lane >> 5)) * ES;
         if (UPGATE) {
           uint16_t hv[4];
 #pragma unroll
@@ -331,16 +337,20 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
           uint2 pk;
           pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
           pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *(uint2*)((uint16_t*)a.out + (int64_t)row * a.ldo + n) = pk;
+          *(uint2*)dst = pk;
         } else {
-          float4 v;
-          v.x = acc[0][i][j][4 * q + 0];
-          v.y = acc[0][i][j][4 * q + 1];
-          v.z = acc[0][i][j][4 * q + 2];
-          v.w = acc[0][i][j][4 * q + 3];
-          *(float4*)((float*)a.out + split * a.split_stride + (int64_t)row * a.ldo + n) = v;
+          *(float4*)dst = make_float4(acc[0][i][j][4 * q + 0], acc[0][i][j][4 * q + 1],
+                                      acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3]);
         }
       }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 32; rr += RPI) {
+      const int r = rr + lane / LPR, cb = (lane % LPR) * 16;
+      const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
+      const int row = row0 + j * 32 + r, col = col0 + cb / ES;
+      if (row < tl.m_end && col < N)
+        *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
     }
   }
 }

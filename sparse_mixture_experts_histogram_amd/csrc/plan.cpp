@@ -83,14 +83,13 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind, d), d->d, d->d);
   // the decode kernels walk a compact list of row tiles (see dispatch.hip)
   P.up.row_list = P.down.row_list = P.kind == KIND_BF16_DECODE;
-  // Schedule order (measured on MI355X): the up/gate GEMM runs chunks of
-  // consecutive entries (row tile fastest) per XCD; the down GEMM (long K, few
-  // column tiles) is faster with column tile fastest and its entries spread
-  // over all XCDs.
+  // Schedule order (measured on MI355X): both GEMMs run chunks of
+  // consecutive entries per XCD; the up/gate GEMM with row tile fastest, the
+  // down GEMM (long K, few column tiles) with column tile fastest.
   P.up.n_fastest = 0;
   P.up.xcd_remap = 1;
   P.down.n_fastest = 1;
-  P.down.xcd_remap = 0;
+  P.down.xcd_remap = 1;
   // A down GEMM with under three tiles per CU loses much of its last round to
   // idle CUs; when its K is long (>= 8192) splitting K in two doubles the
   // tiles at little per-tile cost (the combine adds the two partial outputs in
@@ -104,6 +103,8 @@ int make_plan(const moe_desc* d, Plan* p) {
     const int k_down = std::max(d->ffn, d->n_shared ? d->ffn_shared : 0);
     if (est_tiles < 3 * 256 && k_down >= 8192) P.down.ksplit = 2;
   }
+  // A split down GEMM measured faster with its entries spread over all XCDs.
+  if (P.down.ksplit > 1) P.down.xcd_remap = 0;
 
   const size_t A = 256;
   const size_t eb = d->dtype == MOE_BF16 ? 2 : 4;
