@@ -81,7 +81,8 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
                W.at<void>(P.o_h), out, P.down.ksplit};
   const int64_t part_stride = ((int64_t)P.R + kRowSlack) * d->d;
   MOE_TRY(mark(0));
-  MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank, s));
+  MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank,
+                        W.at<float>(P.o_router_part), s));
   MOE_TRY(mark(1));
   MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
   MOE_TRY(mark(2));
@@ -133,7 +134,7 @@ int moe_route(const moe_desc* d, const void* x, const void* w_router, const floa
   Ws W{(char*)workspace};
   MOE_TRY(launch_router(P, x, w_router, router_bias, topk_idx, topk_w,
                         W.at<int32_t>(P.o_blk_hist), W.at<int32_t>(P.o_blk_rank),
-                        (hipStream_t)stream));
+                        W.at<float>(P.o_router_part), (hipStream_t)stream));
   return MOE_OK;
 }
 

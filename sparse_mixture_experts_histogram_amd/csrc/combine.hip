@@ -4,9 +4,9 @@
 // and VRAM"; shared experts added with weight one per page "Mixture of Experts
 // (MoE): routing, expert parallelism, and memory", section "Shared
 // experts").  A gather per token, no atomics, so the result is deterministic.
-// When the down GEMM split K in two, each expert output row is the sum of its
-// two partial rows, added here in a fixed order.
-// HBM-bound: it reads (k + n_shared) float32 rows (per K part) and writes one
+// When the down GEMM split K (into 2 to 4 ranges), each expert output row is
+// the sum of its partial rows, added here in range order.
+// HBM-bound: it reads (k + n_shared) float32 rows (per K range) and writes one
 // row per token; each workgroup handles one token with 16-byte accesses.
 #include "device.h"
 #include "kernels.h"
@@ -82,10 +82,13 @@ hipError_t launch_combine(const Plan& P, const float* out, int nparts, int64_t p
                        D.E, D.n_shared, y);
   };
   const bool bf = D.y_dtype == MOE_BF16;
-  if (nparts == 2)
-    bf ? go(combine_kernel<true, 2>) : go(combine_kernel<false, 2>);
-  else
-    bf ? go(combine_kernel<true, 1>) : go(combine_kernel<false, 1>);
+  switch (nparts) {
+    case 1: bf ? go(combine_kernel<true, 1>) : go(combine_kernel<false, 1>); break;
+    case 2: bf ? go(combine_kernel<true, 2>) : go(combine_kernel<false, 2>); break;
+    case 3: bf ? go(combine_kernel<true, 3>) : go(combine_kernel<false, 3>); break;
+    case 4: bf ? go(combine_kernel<true, 4>) : go(combine_kernel<false, 4>); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -9,10 +9,11 @@
 namespace moe {
 
 // Router logits + softmax + top-k + renormalise; also writes the per-block
-// histogram and in-block stable ranks of the (token, slot) pairs.
+// histogram and in-block stable ranks of the (token, slot) pairs.  `part`
+// holds the split-K partial logits when P.rsplit > 1.
 hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
-                         hipStream_t s);
+                         float* part, hipStream_t s);
 
 // Per-block histogram and ranks from given top-k indices.
 hipError_t launch_block_hist(const Plan& P, const int32_t* idx, int32_t* blk_hist,

@@ -57,6 +57,16 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.pairs = T * d->k;
   P.R = T * (int64_t)(d->k + d->n_shared);
   P.nblk = cdiv(T, kRouterTokens);
+  // With few token blocks the router's K range is split over up to
+  // kMaxRouterSplit workgroups per block (at least four 32-wide k-steps
+  // each), up to about 256 workgroups.
+  P.rsplit = 1;
+  if (d->dtype == MOE_BF16) {
+    const int64_t nk = d->d / 32;
+    while (P.rsplit < kMaxRouterSplit && P.nblk * P.rsplit * 2 <= 256 &&
+           nk / (P.rsplit * 2) >= 4)
+      P.rsplit *= 2;
+  }
   P.ffn_max = d->n_shared > 0 ? std::max(d->ffn, d->ffn_shared) : d->ffn;
   if (d->path == MOE_PATH_AUTO)
     P.path = (T * d->k <= 8LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
@@ -115,6 +125,8 @@ int make_plan(const moe_desc* d, Plan* p) {
     return at;
   };
   const size_t rows_ws = (size_t)P.R + kRowSlack;
+  const size_t e_pad = (size_t)(d->E + 15) / 16 * 16;
+  P.o_router_part = take(P.rsplit > 1 ? (size_t)P.rsplit * P.nblk * kRouterTokens * e_pad * 4 : 0);
   P.o_blk_hist = take((size_t)P.nblk * d->E * 4);
   P.o_blk_rank = take((size_t)P.pairs * 4);
   P.o_counts = take((size_t)d->E * 4);

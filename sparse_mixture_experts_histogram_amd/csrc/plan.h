@@ -12,6 +12,8 @@ namespace moe {
 
 // Tokens per router workgroup (one block of the per-block histogram).
 constexpr int kRouterTokens = 16;
+// Most workgroups sharing one router block's K range.
+constexpr int kMaxRouterSplit = 16;
 // Largest supported expert count / top-k / shared experts.
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
@@ -47,11 +49,12 @@ struct Plan {
   int64_t R;         // grouped rows = T*(k+n_shared)
   int64_t pairs;     // T*k
   int64_t nblk;      // router blocks
+  int rsplit;        // router workgroups per block (split K; 1 = one kernel)
   int ffn_max;       // max(ffn, ffn_shared)
   int kind;          // kernel family, see KernelKind
   GemmShape up, down;
   // workspace byte offsets
-  size_t o_blk_hist, o_blk_rank, o_counts, o_offsets, o_tiles_up, o_tiles_down, o_sorted,
+  size_t o_router_part, o_blk_hist, o_blk_rank, o_counts, o_offsets, o_tiles_up, o_tiles_down, o_sorted,
       o_slot, o_idx, o_w, o_h, o_out, total;
 };
 

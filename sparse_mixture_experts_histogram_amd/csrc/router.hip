@@ -7,7 +7,8 @@
 // router as one bias-free linear layer per page "Mixture of Experts: why a
 // model with 671 billion parameters uses only 37", section "The router".
 //
-// One workgroup (4 waves) owns kRouterTokens tokens and every expert.  The
+// One workgroup (4 waves) owns kRouterTokens tokens and every expert (with
+// few tokens, several workgroups share a block's K range; see below).  The
 // bf16 variant computes the logit tile with 16x16x32 bf16 MFMAs (exact bf16
 // products, fp32 accumulation); the K range is split across waves when E
 // leaves room for it and the partial tiles are summed in a fixed order.  Selection runs one
@@ -196,6 +197,51 @@ __global__ __launch_bounds__(64 * NW) void router_bf16_kernel(
   router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
 }
 
+// Few token blocks: workgroup b computes the logits of token block
+// b % nblk over K part b / nblk of nsplit and writes them to
+// part[split][token][e] (rows of ep = 16 * expert tiles floats).
+template <int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void router_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E, int KS,
+    int nblk, int nsplit, float* __restrict__ part) {
+  extern __shared__ float lds[];
+  const int ep = ((E + 15) >> 4) * 16, ld = ep + 4;
+  const int blk = blockIdx.x % nblk, split = blockIdx.x / nblk;
+  const int t0 = blk * kRouterTokens, nk = d >> 5;
+  block_logits<NT, NW>(x, wr, T, d, E, KS, t0, split * nk / nsplit, (split + 1) * nk / nsplit,
+                       lds, ld);
+  float* dst = part + ((int64_t)split * nblk * kRouterTokens + t0) * ep;
+  for (int i = threadIdx.x; i < kRouterTokens * ep; i += blockDim.x)
+    dst[i] = lds[(i / ep) * ld + i % ep];
+}
+
+// Adds the nsplit (<= kMaxRouterSplit) partial logits of a token block in
+// split order, then the same selection as the one-kernel router.  All
+// partial loads of an element are issued before the first add, so the sum
+// costs one memory round trip.  Dynamic LDS: [16][ld] floats, then sel[16*k].
+__global__ __launch_bounds__(256) void router_finish_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
+    int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
+  extern __shared__ float lds[];
+  const int ep = ((E + 15) >> 4) * 16, ld = ep + 4;
+  int32_t* sel = (int32_t*)(lds + kRouterTokens * ld);
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int64_t plane = (int64_t)nblk * kRouterTokens * ep;
+  const float* src = part + (int64_t)t0 * ep;
+  for (int i = threadIdx.x; i < kRouterTokens * ep; i += blockDim.x) {
+    float v[kMaxRouterSplit];
+#pragma unroll
+    for (int q = 0; q < kMaxRouterSplit; ++q) v[q] = src[(q < nsplit ? q : 0) * plane + i];
+    float s = v[0];
+#pragma unroll
+    for (int q = 1; q < kMaxRouterSplit; ++q)
+      if (q < nsplit) s += v[q];
+    lds[(i / ep) * ld + i % ep] = s;
+  }
+  __syncthreads();
+  router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+}
+
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
@@ -239,7 +285,7 @@ __global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restri
 
 hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
-                         hipStream_t s) {
+                         float* part, hipStream_t s) {
   const moe_desc& D = P.desc;
   const dim3 grid((unsigned)P.nblk);
   const size_t sel_bytes = (size_t)kRouterTokens * D.k * 4;
@@ -251,9 +297,11 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
     return hipGetLastError();
   }
   // 4 waves; K is split over as many of them as the expert tiles leave free
-  // (KS = 4 / tiles, a power of two), so even one token block keeps all four
-  // streaming the router matrix.  (Measured on MI355X: sixteen waves, or
-  // splitting one block's K range over several workgroups, were slower.)
+  // (KS = 4 / tiles, a power of two).  With few token blocks, K is also
+  // split over P.rsplit workgroups per block and a second kernel adds the
+  // partial logits: one workgroup streaming the whole router matrix pays
+  // one ~2 us memory round trip per batch of loads (measured on MI355X:
+  // gpt-oss-shaped T=1, E=128, d=2880: 28 us in one kernel).
   constexpr int NW = 4;
   const int etiles = (D.E + 15) / 16;
   int KS = NW;
@@ -263,6 +311,27 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
   const size_t lds = (size_t)KS * kRouterTokens * ld * 4 + sel_bytes;
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)w_router;
+  if (P.rsplit > 1) {
+    const dim3 pgrid((unsigned)(P.nblk * P.rsplit));
+    auto partial = [&](auto kern) {
+      hipLaunchKernelGGL(kern, pgrid, dim3(64 * NW), lds, s, xb, wb, (int)D.T, D.d, D.E, KS,
+                         (int)P.nblk, P.rsplit, part);
+    };
+    if (nt <= 1)
+      partial(router_partial_kernel<1, NW>);
+    else if (nt <= 2)
+      partial(router_partial_kernel<2, NW>);
+    else if (nt <= 4)
+      partial(router_partial_kernel<4, NW>);
+    else
+      partial(router_partial_kernel<8, NW>);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(256),
+                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part, bias, (int)D.T, D.E,
+                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank);
+    return hipGetLastError();
+  }
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, s, xb, wb, bias, (int)D.T, D.d, D.E, D.k,
                        KS, idx, w, blk_hist, blk_rank);
