@@ -79,8 +79,11 @@ def upload_layer(cfg, T):
 
 
 def time_forward(x, W, k, steps, warmup):
-    """K timed steps bracketed by synchronize; per-kernel durations from the
-    events each step records on its own launch stream."""
+    """K timed steps of the plain layer call bracketed by synchronize; then
+    as many steps again, untimed by the wall clock, whose per-kernel
+    durations come from the events each step records on its own launch
+    stream (the records themselves cost a few microseconds per step, so they
+    stay out of the timed steps)."""
     import torch
     import sparse_mixture_experts_histogram_amd as moe
     from sparse_mixture_experts_histogram_amd.hipevents import Events
@@ -96,9 +99,12 @@ def time_forward(x, W, k, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+        moe.moe_forward_timed(x, W, k, None, y, ws, counts=counts)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    for i in range(steps):
+        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+    torch.cuda.synchronize()
     names = ["router", "dispatch", "expert_up", "expert_down", "combine"]
     per = {n: statistics.mean(ev.ms(6 * i + j, 6 * i + j + 1) for i in range(steps))
            for j, n in enumerate(names)}
@@ -110,7 +116,11 @@ def time_forward(x, W, k, steps, warmup):
 def time_decode(x, W, k, iters):
     """Per-iteration event timing with L2 and the 256 MB MALL flushed between
     iterations, outside the timed interval, by reading 1 GiB (a read leaves no
-    dirty lines for the next kernel to write back); median."""
+    dirty lines for the next kernel to write back); median.  The layer time
+    comes from iterations that record events only before the first and after
+    the last launch; the expert-GEMM time from a second set that records
+    them between launches too."""
+    import ctypes
     import torch
     import sparse_mixture_experts_histogram_amd as moe
     from sparse_mixture_experts_histogram_amd.hipevents import Events
@@ -122,13 +132,20 @@ def time_decode(x, W, k, iters):
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=x.device)
     flush_sum = torch.empty((), dtype=torch.float32, device=x.device)
     ev = Events(6 * iters)
+    outer = [(ctypes.c_void_p * 6)(ev.ev[6 * i], None, None, None, None, ev.ev[6 * i + 5])
+             for i in range(iters)]
     for _ in range(5):
         moe.moe_forward_timed(x, W, k, None, y, ws, counts=counts)
     for i in range(iters):
         torch.sum(flush, dim=0, out=flush_sum)
-        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+        moe.moe_forward_timed(x, W, k, ctypes.cast(outer[i], ctypes.c_void_p), y, ws,
+                              counts=counts)
     torch.cuda.synchronize()
     layer = statistics.median(ev.ms(6 * i, 6 * i + 5) for i in range(iters))
+    for i in range(iters):
+        torch.sum(flush, dim=0, out=flush_sum)
+        moe.moe_forward_timed(x, W, k, ev.slice(6 * i, 6), y, ws, counts=counts)
+    torch.cuda.synchronize()
     gemm = statistics.median(ev.ms(6 * i + 2, 6 * i + 4) for i in range(iters))
     ev.close()
     del flush
@@ -145,7 +162,8 @@ def decode_leg(cfg, x, W, k, iters):
            "experts_touched": touched, "touched_weight_bytes": touched_bytes,
            "hbm_frac_layer": round(touched_bytes / (dec_layer * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
            "hbm_frac_expert_gemms": round(touched_bytes / (dec_gemm * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
-           "timing": "median of per-iteration hipEvent times, MALL flushed between iterations"}
+           "timing": "median of per-iteration hipEvent times (events before the first and after the "
+                     "last launch only), L2 and MALL flushed by a 1 GiB read between iterations"}
 
     return dec
 

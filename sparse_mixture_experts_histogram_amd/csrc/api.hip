@@ -80,11 +80,16 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
                W.at<void>(P.o_h), out, P.down.ksplit};
   const int64_t part_stride = ((int64_t)P.R + kRowSlack) * d->d;
+  // With a split router and one token block (at most 16 tokens) the router
+  // also runs the dispatch, and events 1 and 2 mark the same point.
+  const bool fused = P.rsplit > 1 && P.nblk == 1;
+  const DispatchOut dout{counts, offsets, sorted, slot, tu, td};
   MOE_TRY(mark(0));
   MOE_TRY(launch_router(P, x, w_router, router_bias, idx, w, blk_hist, blk_rank,
-                        W.at<float>(P.o_router_part), s));
+                        W.at<float>(P.o_router_part), fused ? &dout : nullptr, s));
   MOE_TRY(mark(1));
-  MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
+  if (!fused)
+    MOE_TRY(launch_dispatch(P, idx, blk_hist, blk_rank, counts, offsets, sorted, slot, tu, td, s));
   MOE_TRY(mark(2));
   MOE_TRY(launch_expert_up(P, a, s));
   MOE_TRY(mark(3));
@@ -134,7 +139,7 @@ int moe_route(const moe_desc* d, const void* x, const void* w_router, const floa
   Ws W{(char*)workspace};
   MOE_TRY(launch_router(P, x, w_router, router_bias, topk_idx, topk_w,
                         W.at<int32_t>(P.o_blk_hist), W.at<int32_t>(P.o_blk_rank),
-                        W.at<float>(P.o_router_part), (hipStream_t)stream));
+                        W.at<float>(P.o_router_part), nullptr, (hipStream_t)stream));
   return MOE_OK;
 }
 

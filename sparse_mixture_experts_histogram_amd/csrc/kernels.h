@@ -8,12 +8,20 @@
 
 namespace moe {
 
+// Outputs of the dispatch when the router runs it in the same launch.
+struct DispatchOut {
+  int32_t *counts, *offsets, *sorted_token, *slot_row;
+  Tile *tiles_up, *tiles_down;
+};
+
 // Router logits + softmax + top-k + renormalise; also writes the per-block
 // histogram and in-block stable ranks of the (token, slot) pairs.  `part`
-// holds the split-K partial logits when P.rsplit > 1.
+// holds the split-K partial logits when P.rsplit > 1.  With a split router
+// and a single token block, a non-null `dout` also makes the router run the
+// dispatch (see router.hip); launch_dispatch must then not be called.
 hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
-                         float* part, hipStream_t s);
+                         float* part, const DispatchOut* dout, hipStream_t s);
 
 // Per-block histogram and ranks from given top-k indices.
 hipError_t launch_block_hist(const Plan& P, const int32_t* idx, int32_t* blk_hist,

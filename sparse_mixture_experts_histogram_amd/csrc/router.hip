@@ -19,6 +19,7 @@
 // full softmax (page "Mixture of Experts Explained...", section "Softmax
 // before or after the top-k step").
 #include "device.h"
+#include "dispatch_body.h"
 #include "kernels.h"
 
 namespace moe {
@@ -215,13 +216,28 @@ __global__ __launch_bounds__(64 * NW) void router_partial_kernel(
     dst[i] = lds[(i / ep) * ld + i % ep];
 }
 
+// Where the finish kernel runs the dispatch (null counts: it does not).
+struct FusedDispatch {
+  int32_t *counts, *offsets, *sorted_token, *slot_row;
+  Tile *tiles_up, *tiles_down;
+  TileCfg cu, cd;
+  int n_sh;
+};
+
 // Adds the nsplit (<= kMaxRouterSplit) partial logits of a token block in
 // split order, then the same selection as the one-kernel router.  All
 // partial loads of an element are issued before the first add, so the sum
-// costs one memory round trip.  Dynamic LDS: [16][ld] floats, then sel[16*k].
-__global__ __launch_bounds__(256) void router_finish_kernel(
+// costs one memory round trip.  With a single token block and fd.counts
+// set, the one workgroup then runs the whole dispatch (dispatch_body.h) on
+// the indices, histogram and ranks it has just written, which saves the
+// dispatch launch.  (With several blocks that would take a device-scope
+// fence, which writes back and invalidates L2 and measured slower than the
+// separate launch.)  kDispatchThreads threads; dynamic LDS: [16][ld] floats,
+// then sel[16*k].
+__global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
-    int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
+    int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank,
+    FusedDispatch fd) {
   extern __shared__ float lds[];
   const int ep = ((E + 15) >> 4) * 16, ld = ep + 4;
   int32_t* sel = (int32_t*)(lds + kRouterTokens * ld);
@@ -240,6 +256,10 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
   }
   __syncthreads();
   router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  if (!fd.counts || nblk != 1) return;
+  __syncthreads();  // the workgroup's own global writes are visible to it after the barrier
+  dispatch_body(idx_out, blk_hist, blk_rank, T, k, E, fd.n_sh, nblk, fd.counts, fd.offsets,
+                fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down, fd.cd);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restri
 
 hipError_t launch_router(const Plan& P, const void* x, const void* w_router, const float* bias,
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
-                         float* part, hipStream_t s) {
+                         float* part, const DispatchOut* dout, hipStream_t s) {
   const moe_desc& D = P.desc;
   const dim3 grid((unsigned)P.nblk);
   const size_t sel_bytes = (size_t)kRouterTokens * D.k * 4;
@@ -312,6 +332,12 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)w_router;
   if (P.rsplit > 1) {
+    FusedDispatch fd{};
+    if (dout && P.nblk == 1) {
+      fd = FusedDispatch{dout->counts, dout->offsets, dout->sorted_token, dout->slot_row,
+                         dout->tiles_up, dout->tiles_down, tile_cfg(P.up), tile_cfg(P.down),
+                         D.n_shared};
+    }
     const dim3 pgrid((unsigned)(P.nblk * P.rsplit));
     auto partial = [&](auto kern) {
       hipLaunchKernelGGL(kern, pgrid, dim3(64 * NW), lds, s, xb, wb, (int)D.T, D.d, D.E, KS,
@@ -327,9 +353,9 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
       partial(router_partial_kernel<8, NW>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(256),
+    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
                        (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part, bias, (int)D.T, D.E,
-                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank);
+                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
     return hipGetLastError();
   }
   auto args = [&](auto kern) {
