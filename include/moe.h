@@ -92,7 +92,10 @@ const char* moe_status_str(int status);
  * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
  * n_shared > 0, bad enum, flags != 0, T*(k+n_shared) >= 2^31) or
  * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
- * 64; MOE_F32 with any of them not a multiple of 4). */
+ * 64, or with x (T*d), h ((T*(k+n_shared)+256)*max ffn) or one expert's
+ * weight matrix (max ffn * d) reaching 4 GiB, as the bf16 kernels address
+ * them with 32-bit byte offsets; MOE_F32 with d, ffn or ffn_shared not a
+ * multiple of 4). */
 int moe_validate(const moe_desc* desc);
 
 /* Bytes of workspace every entry point below needs for `desc` (host only). */

@@ -46,6 +46,7 @@ struct GemmArgs {
   int xcd_remap;              // 1: consecutive schedule entries run on one XCD
   int ksplit;                 // K ranges per tile (partial sums to separate outputs)
   int64_t split_stride;       // elements between the outputs of consecutive K ranges
+  uint32_t tok_bytes;         // bytes of tok (the buffer range of its DMA)
 };
 
 constexpr int BK = 64;  // K slab: 8 chunks of 8 bf16 per tile row (one 128-byte line)
@@ -93,13 +94,22 @@ constexpr int kLgkm0 = ~(15 << 8);  // AND into an immediate to also wait lgkmcn
 // global_load_lds_dwordx4 fills bytes [16 l, 16 l + 16) of a block from lane
 // l, so lane l fetches row 8 b + l / 8 at the chunk whose swizzled slot is
 // l % 8: the 8 lanes of a row read its whole 128-byte line.
+// The copies are buffer loads: the operand's base and size sit in a
+// descriptor in scalar registers, each lane adds a 32-bit byte offset (its
+// row and chunk), and the slab's K offset is the scalar offset, so no
+// per-copy address arithmetic or 64-bit address registers are needed.
 template <int NBLK, int NW, int AUX = 0>
-__device__ __forceinline__ void dma_tile(const char* base, const uint32_t* off, uint16_t* lds,
-                                         int wave) {
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t soff,
+                                         const uint32_t* off, uint16_t* lds, int wave) {
 #pragma unroll
   for (int i = 0; i < NBLK; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                     LDS_PTR(lds + (wave + NW * i) * 512), 16, 0, AUX);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds + (wave + NW * i) * 512), 16,
+                                             off[i], soff, 0, AUX);
+}
+
+// Buffer descriptor of `bytes` bytes at p (raw buffer: no stride, no format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
 constexpr int kPolW = 0, kPolX = 0;  // cache policy bits of the weight / token bursts
@@ -168,12 +178,15 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   }
   const int nk_all = K / BK;
   const int kb = split * nk_all / a.ksplit;  // first slab of this K range
+  const uint32_t wbytes = (uint32_t)(wstride * 2);
+  const __amdgpu_buffer_rsrc_t rw0 = buffer_of(W0, wbytes);
+  const __amdgpu_buffer_rsrc_t rw1 = buffer_of(UPGATE ? W1 : W0, wbytes);
+  const __amdgpu_buffer_rsrc_t rx = buffer_of(a.tok, a.tok_bytes);
   auto dma = [&](int kt_local, uint16_t* lw, uint16_t* lx) {
-    const int kt = kb + kt_local;
-    dma_tile<WOFF, NW, kPolW>((const char*)(W0 + kt * BK), woff, lw, wave);
-    if (UPGATE)
-      dma_tile<WOFF, NW, kPolW>((const char*)(W1 + kt * BK), woff, lw + BN * BK, wave);
-    dma_tile<XB, NW, kPolX>((const char*)(a.tok + kt * BK), xoff, lx, wave);
+    const uint32_t koff = (uint32_t)(kb + kt_local) * (BK * 2);
+    dma_tile<WOFF, NW, kPolW>(rw0, koff, woff, lw, wave);
+    if (UPGATE) dma_tile<WOFF, NW, kPolW>(rw1, koff, woff, lw + BN * BK, wave);
+    dma_tile<XB, NW, kPolX>(rx, koff, xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -312,11 +325,12 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   // written through LDS so that every store is a 16-byte piece of a whole
   // row: each wave stages 32 rows x WN features of its tile at a time in a
   // stage buffer of its own (row pitch padded by 16 bytes against bank
-  // conflicts), then 64 / (row bytes / 16) rows per store instruction.
+  // conflicts), then stores them as 16-byte pieces, consecutive lanes along
+  // a row.
   constexpr int ES = UPGATE ? 2 : 4;                  // output element bytes
   constexpr int RB = WN * ES, PITCH = RB + 16;        // staged row bytes, LDS pitch
-  constexpr int LPR = RB / 16, RPI = 64 / LPR;        // lanes per row, rows per store
-  static_assert(NW == 4 && RB % 16 == 0 && 64 % LPR == 0, "epilogue shape");
+  constexpr int LPR = RB / 16;                         // 16-byte pieces per staged row
+  static_assert(NW == 4 && RB % 16 == 0, "epilogue shape");
   static_assert(32 * PITCH <= 2 * (SX < SW ? SX : SW), "staging fits a stage buffer");
   __syncthreads();  // every wave is done reading the stage buffers
   char* st = (char*)(wave == 0 ? lw0 : wave == 1 ? lw1 : wave == 2 ? lx0 : lx1);
@@ -345,12 +359,14 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < 32; rr += RPI) {
-      const int r = rr + lane / LPR, cb = (lane % LPR) * 16;
-      const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
-      const int row = row0 + j * 32 + r, col = col0 + cb / ES;
-      if (row < tl.m_end && col < N)
-        *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
+    for (int id0 = 0; id0 < 32 * LPR; id0 += 64) {
+      const int id = id0 + lane, r = id / LPR, cb = (id % LPR) * 16;
+      if (id < 32 * LPR) {
+        const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
+        const int row = row0 + j * 32 + r, col = col0 + cb / ES;
+        if (row < tl.m_end && col < N)
+          *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
+      }
     }
   }
 }
@@ -573,7 +589,7 @@ static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
   return GemmArgs{(const uint16_t*)x.x, x.sorted_token, D.d, (const uint16_t*)x.w_up,
                   (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
                   (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
-                  x.tiles_up, P.up.xcd_remap, 1, 0};
+                  x.tiles_up, P.up.xcd_remap, 1, 0, (uint32_t)(D.T * D.d * 2)};
 }
 static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
@@ -581,7 +597,8 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   return GemmArgs{(const uint16_t*)x.h, nullptr, P.ffn_max, (const uint16_t*)x.w_down, nullptr,
                   (const uint16_t*)x.ws_down, nullptr, D.E, D.d, D.d, D.ffn, ffn_s, x.out, D.d,
                   x.tiles_down, P.down.xcd_remap, x.ksplit,
-                  (int64_t)((size_t)P.R + kRowSlack) * D.d};
+                  (int64_t)((size_t)P.R + kRowSlack) * D.d,
+                  (uint32_t)(((size_t)P.R + kRowSlack) * P.ffn_max * 2)};
 }
 
 // LDS stages of each prefill GEMM instantiation (at most 160 KB of LDS:

@@ -44,6 +44,15 @@ static int validate(const moe_desc* d) {
   const int q = d->dtype == MOE_BF16 ? 64 : 4;
   if (d->d % q || d->ffn % q) return MOE_ERR_UNSUPPORTED;
   if (d->n_shared > 0 && d->ffn_shared % q) return MOE_ERR_UNSUPPORTED;
+  // The bf16 GEMMs address x, h and each expert's weight matrix with 32-bit
+  // byte offsets.
+  if (d->dtype == MOE_BF16) {
+    const int64_t ffn_max = d->n_shared > 0 ? std::max(d->ffn, d->ffn_shared) : d->ffn;
+    const int64_t lim = int64_t(1) << 32;
+    if (d->T * d->d * 2 >= lim || (rows + kRowSlack) * ffn_max * 2 >= lim ||
+        ffn_max * d->d * 2 >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 

@@ -53,6 +53,11 @@ def test_desc_struct_size():
     (dict(dtype=0, d=36, ffn=20), OK),
     (dict(dtype=0, d=34), UNSUPPORTED),
     (dict(E=512, k=32, d=64, ffn=64), OK),
+    # bf16 operands are addressed with 32-bit byte offsets
+    (dict(T=2 ** 20, d=2048, k=2, ffn=64), UNSUPPORTED),          # x: 4 GiB
+    (dict(T=2 ** 18, d=64, k=2, ffn=4096), UNSUPPORTED),          # h: > 4 GiB
+    (dict(T=64, d=32768, k=2, ffn=65536), UNSUPPORTED),           # one expert: 4 GiB
+    (dict(T=2 ** 20, d=2048, k=2, ffn=64, dtype=0), OK),          # fp32 path: 64-bit offsets
 ])
 def test_validate_codes(kw, code):
     assert moe.moe_validate(desc(**kw)) == code
