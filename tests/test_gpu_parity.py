@@ -40,6 +40,12 @@ SMALL = {c.name: c for c in [
     custom("rows256", 112, T=900, d=192, E=2, k=1, ffn=320),
     # long K and few tiles: the down GEMM splits K in two (partials summed in the combine)
     custom("ksplit", 113, T=200, d=128, E=3, k=2, ffn=8192),
+    # one token block, router K split over workgroups: the router's finish kernel runs
+    # the dispatch itself (with a shared expert and a logit bias)
+    custom("fused_dispatch", 114, T=13, d=512, E=64, k=6, ffn=128, n_shared=1, ffn_shared=192,
+           bias="normal", bias_var=0.5),
+    # several token blocks with the router K split over workgroups, two shared experts
+    custom("split_router", 115, T=100, d=512, E=16, k=2, ffn=64, n_shared=2, ffn_shared=64),
     NAMED["tiny_f32"],
 ]}
 
