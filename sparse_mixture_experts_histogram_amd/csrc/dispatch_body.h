@@ -19,8 +19,8 @@
 //      stable grouping (pairs of one expert keep increasing t*k+j order);
 //   5. fills the shared groups' rows with tokens 0..T-1.
 // Everything is integer work and deterministic.  The body is a device
-// function so that the router's last workgroup can run it when the router
-// and the dispatch share one launch (few tokens).
+// function so that the router's finish kernel can run it when there is a
+// single token block (the router and the dispatch then share one launch).
 #pragma once
 #include "device.h"
 #include "kernels.h"
