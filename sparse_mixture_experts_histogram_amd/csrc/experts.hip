@@ -114,7 +114,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint3
 
 constexpr int kPolW = 0, kPolX = 0;  // cache policy bits of the weight / token bursts
 constexpr int kSpread = 2;            // k-steps of a slab over which its DMAs are issued
-template <int BM, int BN, int WM, int WN, bool UPGATE, int NST>
+template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX>
 __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WROWS = UPGATE ? 2 * BN : BN;        // weight rows in the tile
   constexpr int NWN = BN / WN, NWM = BM / WM;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   constexpr int XB = BM / (8 * NW);
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
-  static_assert(NST == 2 || NST == 3, "stages");
+  static_assert(NSW >= 2 && NSW <= 3 && NSX >= 2 && NSX <= 3, "stages");
 
   // With a K split, entries [q*count, (q+1)*count) run K range q of every
   // tile and write their partial sums to output q.
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   const uint16_t* W1 = UPGATE ? (sh ? a.s1 + (tl.g - a.E) * wstride : a.w1 + tl.g * wstride)
                               : nullptr;
 
-  // NST stage buffers per operand, as separate arrays so the compiler can
-  // tell reads of one buffer from DMA still landing in another (an unused
-  // third one is a token 16 bytes).
+  // NSW weight and NSX token stage buffers, as separate arrays so the
+  // compiler can tell reads of one buffer from DMA still landing in another
+  // (an unused third one is a token 16 bytes).
   constexpr int SW = WROWS * BK, SX = BM * BK;
-  __shared__ __attribute__((aligned(1024))) uint16_t lw0[SW], lw1[SW], lw2[NST > 2 ? SW : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lx0[SX], lx1[SX], lx2[NST > 2 ? SX : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lw0[SW], lw1[SW], lw2[NSW > 2 ? SW : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lx0[SX], lx1[SX], lx2[NSX > 2 ? SX : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,11 +182,27 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   const __amdgpu_buffer_rsrc_t rw0 = buffer_of(W0, wbytes);
   const __amdgpu_buffer_rsrc_t rw1 = buffer_of(UPGATE ? W1 : W0, wbytes);
   const __amdgpu_buffer_rsrc_t rx = buffer_of(a.tok, a.tok_bytes);
-  auto dma = [&](int kt_local, uint16_t* lw, uint16_t* lx) {
-    const uint32_t koff = (uint32_t)(kb + kt_local) * (BK * 2);
-    dma_tile<WOFF, NW, kPolW>(rw0, koff, woff, lw, wave);
-    if (UPGATE) dma_tile<WOFF, NW, kPolW>(rw1, koff, woff, lw + BN * BK, wave);
-    dma_tile<XB, NW, kPolX>(rx, koff, xoff, lx, wave);
+  // Ring turns and leading zero slabs.  A turn is lcm(NSW, NSX) slabs.  The
+  // 3 + 3 ring prepends zero slabs up to a whole number of turns: their
+  // copies go through a descriptor of size 0, which reads as zeros, so they
+  // add nothing.  (A separate code path for a partial turn made the compiler
+  // add a full drain at the top of its loop.)  The other rings run the
+  // slabs left over after whole turns as straight-line code.
+  constexpr int P = NSW == NSX ? NSW : NSW * NSX;
+  constexpr bool kPadTurns = NSW == 3 && NSX == 3;
+  const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
+  const int pad = kPadTurns ? (P - nk % P) % P : 0;
+  const __amdgpu_buffer_rsrc_t rzero = buffer_of(W0, 0);
+  auto dma_w = [&](int kt_local, uint16_t* lw) {
+    const int s = kt_local - pad;
+    const uint32_t koff = s < 0 ? 0u : (uint32_t)(kb + s) * (BK * 2);
+    dma_tile<WOFF, NW, kPolW>(s < 0 ? rzero : rw0, koff, woff, lw, wave);
+    if (UPGATE) dma_tile<WOFF, NW, kPolW>(s < 0 ? rzero : rw1, koff, woff, lw + BN * BK, wave);
+  };
+  auto dma_x = [&](int kt_local, uint16_t* lx) {
+    const int s = kt_local - pad;
+    const uint32_t koff = s < 0 ? 0u : (uint32_t)(kb + s) * (BK * 2);
+    dma_tile<XB, NW, kPolX>(s < 0 ? rzero : rx, koff, xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -249,74 +265,140 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Wait until at most n slabs' DMA of this wave are outstanding (and every
+  // Every slab issues the weight DMA of slab J + NSW - 1 and the token DMA
+  // of slab J + NSX - 1 (clamped to the last slab: near the end it
+  // re-fetches into a buffer nothing reads any more), the operand with the
+  // shorter ring first.  Before reading slab J + 1 a wave waits until that
+  // slab's copies have landed; the copies issued after the later of the two
+  // may stay in flight.
+  static_assert(NSX <= NSW, "the token ring is never the longer one");
+  constexpr int NWI = (UPGATE ? 2 : 1) * WOFF;  // weight copies per slab
+  constexpr int WAIT = NSX == NSW ? (NSW - 2) * NDMA : NWI + (NSW - NSX - 1) * NDMA;
+  static_assert(WAIT <= 63, "vmcnt range");
+  auto dma = [&](int kt_w, uint16_t* lw, int kt_x, uint16_t* lx) {
+    if constexpr (NSX < NSW) {
+      dma_x(kt_x, lx);
+      dma_w(kt_w, lw);
+    } else {
+      dma_w(kt_w, lw);
+      dma_x(kt_x, lx);
+    }
+  };
+  // Wait until this wave's copies of the next slab have landed (and every
   // fragment read is done), then for all waves.
-  auto wait_slabs = [&](int n) {
+  auto wait_next = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    if (n > 0)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA) & kLgkm0);
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & kLgkm0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT) & kLgkm0);
     barrier();
   };
 
-  const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
-  // The first nk % NST slabs go through buffer 0 one at a time, so the ring
-  // below always runs a whole number of NST-slab turns.
-  const int r0 = nk % NST;
-  for (int kt = 0; kt < r0; ++kt) {
-    dma(kt, lw0, lx0);
-    wait_slabs(0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      fload(lw0, lx0, kk, fxA, fwA);
-      mfmas(fxA, fwA);
-    }
-    wait_slabs(0);
-  }
-  const int m = nk - r0;
+  const int m = nk + pad;  // slabs to run
+  // Ring buffer i of each operand (i a constant, so the named array is used
+  // directly and the compiler keeps telling the stages apart).
+#define MOE_WB(i) ((i) == 0 ? lw0 : (i) == 1 ? lw1 : lw2)
+#define MOE_XB(i) ((i) == 0 ? lx0 : (i) == 1 ? lx1 : lx2)
   if (m > 0) {
-    dma(r0 + 0, lw0, lx0);
-    if (NST > 2) dma(r0 + 1, lw1, lx1);
-    wait_slabs(NST - 2);
-    fload(lw0, lx0, 0, fxA, fwA);
-    // One slab of four k-steps: DMA the slab NST - 1 ahead into the buffer
-    // freed last slab; each k-step's MFMAs run while the next k-step's
-    // fragments are read; before the last k-step's MFMAs, wait until the
-    // next slab has landed and read its first fragments.  No branches, so
-    // each stretch between barriers is one scheduling region: near the end
-    // the DMA re-fetches the last slab into a buffer nothing reads any more,
-    // and the final next-slab read is simply unused.
-#define MOE_SLAB(J, LWC, LXC, LWN, LXN, LWT, LXT)    \
-    {                                                \
-      dma(r0 + min((J) + NST - 1, m - 1), LWT, LXT); \
-      fload(LWC, LXC, 1, fxB, fwB);                  \
-      mfmas(fxA, fwA);                               \
-      pipeline(ND0);                                 \
-      fload(LWC, LXC, 2, fxA, fwA);                  \
-      mfmas(fxB, fwB);                               \
-      pipeline(ND1);                                 \
-      fload(LWC, LXC, 3, fxB, fwB);                  \
-      mfmas(fxA, fwA);                               \
-      pipeline(ND2);                                 \
-      wait_slabs(NST - 2);                           \
-      fload(LWN, LXN, 0, fxA, fwA);                  \
-      mfmas(fxB, fwB);                               \
-      pipeline(0);                                   \
-    }
-    if constexpr (NST == 2) {
-      for (int j = 0; j < m; j += 2) {
-        MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw1, lx1)
-        MOE_SLAB(j + 1, lw1, lx1, lw0, lx0, lw0, lx0)
-      }
+    // Copies of the slabs before 0, in the order a slab issues them.
+    // (Slab -2 exists only for a 3-stage weight ring; slab -1 copies the
+    // tokens of slab 0 or 1 and the weights of slab 0 or 1.)
+    if constexpr (NSW == 3 && NSX == 2) {
+      dma_w(0, lw0);
+      dma(min(1, m - 1), lw1, 0, lx0);
+    } else if constexpr (NSW == 3) {
+      dma(0, lw0, 0, lx0);
+      dma(min(1, m - 1), lw1, min(1, m - 1), lx1);
     } else {
-      for (int j = 0; j < m; j += 3) {
-        MOE_SLAB(j + 0, lw0, lx0, lw1, lx1, lw2, lx2)
-        MOE_SLAB(j + 1, lw1, lx1, lw2, lx2, lw0, lx0)
-        MOE_SLAB(j + 2, lw2, lx2, lw0, lx0, lw1, lx1)
-      }
+      dma(0, lw0, 0, lx0);
     }
+    wait_next();
+    fload(lw0, lx0, 0, fxA, fwA);
+    // One slab of four k-steps in ring position Q (weights in wr[Q % NSW],
+    // tokens in xr[Q % NSX]): issue the copies ahead; each k-step's MFMAs run
+    // while the next k-step's fragments are read; before the last k-step's
+    // MFMAs, wait until the next slab has landed and read its first
+    // fragments.  No branches inside, so each stretch between barriers is one
+    // scheduling region; the final next-slab read of the layer is unused.
+#define MOE_SLAB(J, Q)                                                    \
+    {                                                                       \
+      dma(min((J) + NSW - 1, m - 1), MOE_WB(((Q) + NSW - 1) % NSW),         \
+          min((J) + NSX - 1, m - 1), MOE_XB(((Q) + NSX - 1) % NSX));        \
+      fload(MOE_WB((Q) % NSW), MOE_XB((Q) % NSX), 1, fxB, fwB);             \
+      mfmas(fxA, fwA);                                                      \
+      pipeline(ND0);                                                        \
+      fload(MOE_WB((Q) % NSW), MOE_XB((Q) % NSX), 2, fxA, fwA);             \
+      mfmas(fxB, fwB);                                                      \
+      pipeline(ND1);                                                        \
+      fload(MOE_WB((Q) % NSW), MOE_XB((Q) % NSX), 3, fxB, fwB);             \
+      mfmas(fxA, fwA);                                                      \
+      pipeline(ND2);                                                        \
+      wait_next();                                                          \
+      fload(MOE_WB(((Q) + 1) % NSW), MOE_XB(((Q) + 1) % NSX), 0, fxA, fwA); \
+      mfmas(fxB, fwB);                                                      \
+      pipeline(0);                                                          \
+    }
+    // Whole turns of both rings, then the m % P slabs left over as the first
+    // positions of one more turn.  Each remainder gets its own straight-line
+    // copy: a shared tail with a branch after every slab made the compiler
+    // spill the accumulators.  (Always whole turns with leading zero slabs.)
+#define MOE_TURNS                                     \
+    for (int j = 0; j < mt; j += P) {                   \
+      MOE_SLAB(j, 0)                                    \
+      MOE_SLAB(j + 1, 1)                                \
+      if constexpr (P >= 3) MOE_SLAB(j + 2, 2)          \
+      if constexpr (P == 6) {                           \
+        MOE_SLAB(j + 3, 3)                              \
+        MOE_SLAB(j + 4, 4)                              \
+        MOE_SLAB(j + 5, 5)                              \
+      }                                                 \
+    }
+    const int mr = kPadTurns ? 0 : m % P, mt = m - mr;
+    switch (mr) {
+      case 0:
+        MOE_TURNS
+        break;
+      case 1:
+        MOE_TURNS
+        MOE_SLAB(mt, 0)
+        break;
+      case 2:
+        if constexpr (P > 2) {
+          MOE_TURNS
+          MOE_SLAB(mt, 0)
+          MOE_SLAB(mt + 1, 1)
+        }
+        break;
+      case 3:
+        if constexpr (P > 3) {
+          MOE_TURNS
+          MOE_SLAB(mt, 0)
+          MOE_SLAB(mt + 1, 1)
+          MOE_SLAB(mt + 2, 2)
+        }
+        break;
+      case 4:
+        if constexpr (P > 4) {
+          MOE_TURNS
+          MOE_SLAB(mt, 0)
+          MOE_SLAB(mt + 1, 1)
+          MOE_SLAB(mt + 2, 2)
+          MOE_SLAB(mt + 3, 3)
+        }
+        break;
+      default:
+        if constexpr (P > 5) {
+          MOE_TURNS
+          MOE_SLAB(mt, 0)
+          MOE_SLAB(mt + 1, 1)
+          MOE_SLAB(mt + 2, 2)
+          MOE_SLAB(mt + 3, 3)
+          MOE_SLAB(mt + 4, 4)
+        }
+        break;
+    }
+#undef MOE_TURNS
 #undef MOE_SLAB
+#undef MOE_WB
+#undef MOE_XB
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
   }
 
@@ -601,18 +683,22 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
                   (uint32_t)(((size_t)P.R + kRowSlack) * P.ffn_max * 2)};
 }
 
-// LDS stages of each prefill GEMM instantiation (at most 160 KB of LDS:
-// 64 KB per stage for 256x256-row tiles, 48 KB for 128-row tiles).
-constexpr int kStagesUp128 = 3, kStagesUp256 = 2, kStagesDown128 = 3, kStagesDown256 = 2;
+// LDS stages (weights, tokens) of the prefill GEMM instantiations, at most
+// 160 KB: 256-row tiles hold 3 x 32 KB of weight slabs and 2 x 32 KB of
+// token slabs when K has at least kDeepRingSlabs slabs (measured on MI355X,
+// Mixtral-shaped T=4096 layer: 2.93 ms with 2 + 2 stages, 2.62 ms with
+// 3 + 2), else 2 + 2; 128-row tiles 3 x (32 + 16) KB.
+constexpr int kWStages256 = 3, kXStages256 = 2, kWStages128 = 3, kXStages128 = 3;
+constexpr int kDeepRingSlabs = 32;
 // Per-wave tile (rows x output columns) of the 256-row instantiations; the
 // wave count is (BM / WM) * (BN / WN).
 constexpr int kUp256WM = 128, kUp256WN = 64, kDown256WM = 128, kDown256WN = 128;
 
-template <int BM, int BN, int WM, int WN, bool UPGATE, int NST>
+template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX>
 static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   constexpr int nw = (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NST>), grid, dim3(64 * nw), 0, s,
-                     a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX>), grid, dim3(64 * nw), 0,
+                     s, a);
 }
 
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
@@ -630,9 +716,11 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
-    launch_gemm<128, 128, 128, 32, true, kStagesUp128>(grid, s, up_args(P, x));
+    launch_gemm<128, 128, 128, 32, true, kWStages128, kXStages128>(grid, s, up_args(P, x));
+  else if (D.d / 64 >= kDeepRingSlabs)
+    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x));
   else
-    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kStagesUp256>(grid, s, up_args(P, x));
+    launch_gemm<256, 128, kUp256WM, kUp256WN, true, 2, 2>(grid, s, up_args(P, x));
   return hipGetLastError();
 }
 
@@ -651,9 +739,12 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
   if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
-    launch_gemm<128, 256, 128, 64, false, kStagesDown128>(grid, s, down_args(P, x));
+    launch_gemm<128, 256, 128, 64, false, kWStages128, kXStages128>(grid, s, down_args(P, x));
+  else if (std::max(D.ffn, D.n_shared ? D.ffn_shared : 0) / 64 / x.ksplit >= kDeepRingSlabs)
+    launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(grid, s,
+                                                                                  down_args(P, x));
   else
-    launch_gemm<256, 256, kDown256WM, kDown256WN, false, kStagesDown256>(grid, s, down_args(P, x));
+    launch_gemm<256, 256, kDown256WM, kDown256WN, false, 2, 2>(grid, s, down_args(P, x));
   return hipGetLastError();
 }
 
