@@ -685,11 +685,10 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
 
 // LDS stages (weights, tokens) of the prefill GEMM instantiations, at most
 // 160 KB: 256-row tiles hold 3 x 32 KB of weight slabs and 2 x 32 KB of
-// token slabs when K has at least kDeepRingSlabs slabs (measured on MI355X,
-// Mixtral-shaped T=4096 layer: 2.93 ms with 2 + 2 stages, 2.62 ms with
-// 3 + 2), else 2 + 2; 128-row tiles 3 x (32 + 16) KB.
+// token slabs, 128-row tiles 3 x (32 + 16) KB.  Measured on MI355X against
+// 2 + 2 stages for 256-row tiles: Mixtral-shaped T=4096 layer 2.93 -> 2.62
+// ms; a 16-slab down GEMM 0.116 -> 0.109 ms.
 constexpr int kWStages256 = 3, kXStages256 = 2, kWStages128 = 3, kXStages128 = 3;
-constexpr int kDeepRingSlabs = 32;
 // Per-wave tile (rows x output columns) of the 256-row instantiations; the
 // wave count is (BM / WM) * (BN / WN).
 constexpr int kUp256WM = 128, kUp256WN = 64, kDown256WM = 128, kDown256WN = 128;
@@ -717,10 +716,8 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
     launch_gemm<128, 128, 128, 32, true, kWStages128, kXStages128>(grid, s, up_args(P, x));
-  else if (D.d / 64 >= kDeepRingSlabs)
-    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x));
   else
-    launch_gemm<256, 128, kUp256WM, kUp256WN, true, 2, 2>(grid, s, up_args(P, x));
+    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x));
   return hipGetLastError();
 }
 
@@ -740,11 +737,9 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
     launch_gemm<128, 256, 128, 64, false, kWStages128, kXStages128>(grid, s, down_args(P, x));
-  else if (std::max(D.ffn, D.n_shared ? D.ffn_shared : 0) / 64 / x.ksplit >= kDeepRingSlabs)
+  else
     launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(grid, s,
                                                                                   down_args(P, x));
-  else
-    launch_gemm<256, 256, kDown256WM, kDown256WN, false, 2, 2>(grid, s, down_args(P, x));
   return hipGetLastError();
 }
 
