@@ -30,6 +30,26 @@ notes of the repository):
 * a per-expert bias, when present, is added to the logits before the softmax;
 * shared experts are added with coefficient one; no residual term is added.
 
+Router variants (not the default layer; selected by arguments):
+
+* sigmoid scoring (P2 "How many experts to pick and how to score them: top-k,
+  softmax, sigmoid"): each expert's score is sigmoid(logit) on its own; the
+  per-expert balancing bias (P2 "The problem learned routing brings: load
+  balancing"; P3 "Why load balancing is the hard part of MoE": the bias moves
+  routing but not the gate values) is added to the scores for selection only;
+  the weights are the kept scores, renormalised over the kept set;
+* raw weights (P4 "Why top-1 routing cannot renormalise"): the kept scores
+  (softmax probabilities over all experts, or sigmoid scores) are used as they
+  are, without renormalising;
+* expert capacity (P2 "Capacity factor: when tokens don't fit"; P4, the
+  capacity passage after the balance-loss example in "Noise and the second
+  expert"): capacity = ceil(T*k/E * factor), the P4 form over routing slots
+  (P2 writes tokens per batch over experts; with top-k each token fills k
+  slots); each expert takes the first `capacity` (token, slot) pairs that
+  chose it in pair order t*k+j, and a pair beyond that skips the expert, so
+  its term is missing from y (the token would pass on through the residual
+  connection, which this layer does not add).
+
 Parity status: every function here is pinned by a CPU test against the pages'
 printed worked example, closed forms, brute force or a library routine, except
 the Zipf bias calibration in ``make_input_tables.py``, whose outcome is an
@@ -37,6 +57,7 @@ input recipe and is parity unpinned.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Callable, Optional, Sequence, Tuple
 
@@ -90,13 +111,66 @@ def renormalise(P: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return kept / kept.sum(axis=-1, keepdims=True)
 
 
-def route(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int):
-    """Router: logits, probabilities, top-k indices and renormalised weights."""
-    L = router_logits(x, w_router, bias)
-    P = softmax(L)
-    idx = select_topk(L, k)
-    w = renormalise(P, idx)
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Independent per-expert score in (0, 1): 1 / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def kept_scores(P: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """The scores of the k kept experts, as they are (no renormalising)."""
+    return np.take_along_axis(P, idx.astype(np.int64), axis=-1)
+
+
+def selection_keys(L: np.ndarray, P: np.ndarray, bias: Optional[np.ndarray],
+                   scoring: str) -> np.ndarray:
+    """What the top-k step ranks.  softmax: the logits (bias already in L).
+    sigmoid: the scores plus the per-expert bias, which only steers the
+    choice."""
+    if scoring == "softmax":
+        return L
+    if scoring == "sigmoid":
+        return P if bias is None else P + np.asarray(bias, np.float64)[None, :]
+    raise ValueError(scoring)
+
+
+def route(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int,
+          scoring: str = "softmax", renormalize: bool = True):
+    """Router: logits L, per-expert scores P (softmax probabilities, or
+    sigmoid scores), top-k indices and weights.  Softmax scoring adds the bias
+    to the logits; sigmoid scoring leaves it out of L and P and adds it to the
+    selection keys only.  Weights are the kept scores, renormalised unless
+    ``renormalize`` is false."""
+    if scoring == "softmax":
+        L = router_logits(x, w_router, bias)
+        P = softmax(L)
+    elif scoring == "sigmoid":
+        L = router_logits(x, w_router, None)
+        P = sigmoid(L)
+    else:
+        raise ValueError(scoring)
+    idx = select_topk(selection_keys(L, P, bias, scoring), k)
+    w = renormalise(P, idx) if renormalize else kept_scores(P, idx)
     return L, P, idx, w
+
+
+def expert_capacity(T: int, k: int, E: int, factor: float) -> int:
+    """Most (token, slot) pairs one expert takes: ceil(T*k/E * factor),
+    evaluated in that order in IEEE double (P4's capacity line)."""
+    return math.ceil(T * k / E * factor)
+
+
+def capacity_keep(idx: np.ndarray, E: int, capacity: int) -> np.ndarray:
+    """bool [T,k]: pair (t, j) is kept when fewer than `capacity` pairs with a
+    smaller pair id t'*k+j' chose the same expert."""
+    idx = np.asarray(idx)
+    flat = idx.ravel()
+    taken = np.zeros(E, dtype=np.int64)
+    keep = np.zeros(flat.shape, dtype=bool)
+    for p, e in enumerate(flat.tolist()):
+        keep[p] = taken[e] < capacity
+        taken[e] += 1
+    return keep.reshape(idx.shape)
 
 
 def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
@@ -162,6 +236,7 @@ class MoEResult:
     logits: np.ndarray     # [T, E] float64
     probs: np.ndarray      # [T, E] float64
     tokens: np.ndarray     # token ids y covers
+    keep: np.ndarray       # [T, k] bool: pair taken by its expert (all True without capacity)
 
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -170,7 +245,9 @@ ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
 def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int,
                 expert_fn: ExpertFn, E: int, dtype: str,
                 shared_fn: Optional[ExpertFn] = None, n_shared: int = 0,
-                tokens: Optional[Sequence[int]] = None) -> MoEResult:
+                tokens: Optional[Sequence[int]] = None, scoring: str = "softmax",
+                renormalize: bool = True,
+                capacity_factor: Optional[float] = None) -> MoEResult:
     """The whole layer (P4 step "Run and combine"; P1 "Shared experts"):
 
         y[t] = sum_{j<k} w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])
@@ -182,11 +259,18 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
     expert_fn(e) / shared_fn(s) return the stored (W_up, W_gate, W_down) of an
     expert.  Routing is computed for all T tokens; y only for ``tokens``
     (default: all), so large layers can be checked on a sample.
+    ``scoring`` / ``renormalize`` pick the router variant (see ``route``);
+    with a ``capacity_factor`` the pairs beyond an expert's capacity (which
+    depends on every token's routing) add nothing to y.
     """
     X = widen(x, dtype)
-    L, P, idx, w = route(X, widen(w_router, dtype), bias, k)
+    L, P, idx, w = route(X, widen(w_router, dtype), bias, k, scoring, renormalize)
     T = X.shape[0]
     counts = expert_counts(idx, E)
+    if capacity_factor is None:
+        keep = np.ones(idx.shape, dtype=bool)
+    else:
+        keep = capacity_keep(idx, E, expert_capacity(T, k, E, capacity_factor))
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     # per (sampled token, slot) expert output, then a slot-ordered sum
     slot_out = np.zeros((len(tok), k, X.shape[1]))
@@ -205,9 +289,10 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
         slot_out[rows, pairs % k] = out
     y = np.zeros((len(tok), X.shape[1]))
     wt = w[tok]
+    kt = keep[tok]
     for j in range(k):
-        y += wt[:, j:j + 1] * slot_out[:, j]
+        y += np.where(kt[:, j:j + 1], wt[:, j:j + 1] * slot_out[:, j], 0.0)
     for s in range(n_shared):
         su, sg, sd = (widen(a, dtype) for a in shared_fn(s))
         y += swiglu_expert(X[tok], su, sg, sd)
-    return MoEResult(y, idx, w, counts, L, P, tok)
+    return MoEResult(y, idx, w, counts, L, P, tok, keep)

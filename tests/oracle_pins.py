@@ -245,7 +245,170 @@ def check_occupancy_monte_carlo(trials=3000, seed=7):
         assert abs(shares.mean() - om.share_touched(k, E, B)) < 4 * se + 1e-12, (k, E, B)
 
 
+# ---------------------------------------------------------------- router variants
+def check_sigmoid_library():
+    z = np.linspace(-60, 60, 1201)
+    assert np.max(np.abs(om.sigmoid(z) - scipy.special.expit(z))) < 1e-15
+    assert om.sigmoid(np.array([0.0]))[0] == 0.5
+
+
+def check_sigmoid_bias_selection_only():
+    """Closed forms of sigmoid scoring with a selection-only bias: the bias
+    decides which experts are kept, the weights use the scores alone."""
+    x = np.eye(3)
+    wr = np.array([[3.0, 0.0, 0.0], [0.0, 0.0, 0.0], [0.0, 0.0, 0.0]])  # L = [3, 0, 0] for token 0
+    b = np.array([0.0, 0.5, 0.25])
+    L, S, idx, w = om.route(x[:1], wr, b, 1, scoring="sigmoid")
+    assert L[0].tolist() == [3.0, 0.0, 0.0]                  # no bias in the logits
+    assert idx[0].tolist() == [1]                            # 0.5 + 0.5 > 1/(1+e^-3) > 0.5 + 0.25
+    assert w[0].tolist() == [1.0]
+    _, _, idx2, w2 = om.route(x[:1], wr, b, 2, scoring="sigmoid")
+    s3 = 1.0 / (1.0 + math.exp(-3.0))
+    assert idx2[0].tolist() == [1, 0]
+    assert np.allclose(w2[0], [0.5 / (0.5 + s3), s3 / (0.5 + s3)], rtol=0, atol=1e-15)
+    _, _, idx3, w3 = om.route(x[:1], wr, b, 2, scoring="sigmoid", renormalize=False)
+    assert idx3[0].tolist() == [1, 0] and np.allclose(w3[0], [0.5, s3], rtol=0, atol=1e-15)
+    # without a bias the choice is the logit order (sigmoid is increasing)
+    _, _, idx4, _ = om.route(x[:1], wr, None, 3, scoring="sigmoid")
+    assert idx4[0].tolist() == [0, 1, 2]
+
+
+def check_sigmoid_routing_bruteforce(seed=21, T=150, d=10, E=7, k=3):
+    """Sigmoid routing against brute force over all k-subsets: the kept set
+    maximises the sum of (expit(logit) + bias), listed by decreasing key; the
+    weights are library expit scores over that set, renormalised or raw."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / np.sqrt(d) * 3
+    b = rng.standard_normal(E) * 0.3
+    L, S, idx, w = om.route(x, wr, b, k, scoring="sigmoid")
+    _, _, idx_r, w_r = om.route(x, wr, b, k, scoring="sigmoid", renormalize=False)
+    Lref = x @ wr.T
+    sref = scipy.special.expit(Lref)
+    assert np.max(np.abs(L - Lref)) < 1e-12
+    for t in range(T):
+        key = sref[t] + b
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(key[list(c)]))
+        order = sorted(best, key=lambda e: -key[e])
+        assert idx[t].tolist() == order and idx_r[t].tolist() == order
+        kept = sref[t, order]
+        assert np.max(np.abs(w[t] - kept / kept.sum())) < 1e-14
+        assert np.max(np.abs(w_r[t] - kept)) < 1e-15
+
+
+def check_raw_softmax_weights(seed=22, T=80, d=12, E=6):
+    """Raw weights under softmax scoring are the library softmax probabilities
+    of the kept experts; with k = E they sum to one; renormalised top-1
+    weights are exactly one (P4 "Why top-1 routing cannot renormalise")."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    b = rng.standard_normal(E)
+    Pref = scipy.special.softmax(x @ wr.T + b, axis=1)
+    for k in (1, 3, E):
+        _, _, idx, w = om.route(x, wr, b, k, renormalize=False)
+        assert np.max(np.abs(w - np.take_along_axis(Pref, idx.astype(np.int64), axis=1))) < 1e-15
+        if k == E:
+            assert np.max(np.abs(w.sum(axis=1) - 1)) < 1e-14
+        _, _, _, wn = om.route(x, wr, b, k)
+        if k == 1:
+            assert np.all(wn == 1.0)
+
+
+def check_capacity_closed_forms():
+    """P4's capacity line: ceil(tokens * k / experts * factor).  On the page's
+    printed tokens-per-expert list (512 tokens, top-2, 8 experts) factor 1.0
+    gives 128 and drops (135-128)+(147-128)+(133-128) = 31 slots; factors 1.25
+    and 2.0 drop none (the page: an even router drops nothing at 1.25)."""
+    G = golden("worked_example_routing.json")
+    counts = np.array(G["tokens_per_expert"])
+    assert om.expert_capacity(512, 2, 8, 1.0) == 128
+    assert om.expert_capacity(512, 2, 8, 1.25) == 160
+    assert om.expert_capacity(512, 2, 8, 2.0) == 256
+    assert om.expert_capacity(10, 2, 3, 1.0) == 7       # 6.67 rounds up
+    assert om.expert_capacity(3, 1, 4, 0.5) == 1        # 0.375 rounds up
+    # pairs in an order that has the printed counts: expert of pair p
+    flat = np.repeat(np.arange(8), counts)
+    rng = np.random.default_rng(23)
+    rng.shuffle(flat)
+    idx = flat.reshape(512, 2)
+    for factor, dropped in ((1.0, 7 + 19 + 5), (1.25, G["capacity_factor_1_25_dropped"]), (2.0, 0)):
+        keep = om.capacity_keep(idx, 8, om.expert_capacity(512, 2, 8, factor))
+        assert int((~keep).sum()) == dropped, factor
+
+
+def _keep_by_sort(idx, E, cap):
+    """Independent form of the capacity rule: stable-sort the pairs by expert;
+    a pair is kept when its position inside its expert's run is below cap."""
+    flat = np.asarray(idx).ravel()
+    order = np.argsort(flat, kind="stable")
+    starts = np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))[:-1]])
+    pos = np.empty(len(flat), dtype=np.int64)
+    pos[order] = np.arange(len(flat)) - starts[flat[order]]
+    return (pos < cap).reshape(np.asarray(idx).shape)
+
+
+def check_capacity_bruteforce(seed=24):
+    """Capacity keep-mask against the sort-based form, per-expert kept counts
+    min(count, capacity), and every dropped pair after every kept pair of its
+    expert; then y against a dense evaluation with the dropped gates zeroed."""
+    rng = np.random.default_rng(seed)
+    for T, E, k, factor in ((40, 5, 2, 1.0), (64, 8, 3, 0.6), (7, 3, 3, 2.0), (50, 6, 1, 0.25)):
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if k > 1 else \
+            rng.integers(0, 2, size=(T, 1))  # skewed: experts 0 and 1 only
+        cap = om.expert_capacity(T, k, E, factor)
+        keep = om.capacity_keep(idx, E, cap)
+        assert np.array_equal(keep, _keep_by_sort(idx, E, cap)), (T, E, k, factor)
+        counts = np.bincount(idx.ravel(), minlength=E)
+        kept = np.bincount(idx.ravel()[keep.ravel()], minlength=E)
+        assert np.array_equal(kept, np.minimum(counts, cap))
+        for e in range(E):
+            ks = keep.ravel()[idx.ravel() == e]
+            assert np.all(np.diff(ks.astype(int)) <= 0)
+    # the whole layer: skewed router so some pairs drop
+    T, d, E, k, f = 30, 10, 4, 2, 12
+    x, wr, b, ex, sh = rand_layer(25, T, d, E, k, f, n_shared=1, f_sh=8)
+    b = np.array([2.0, 1.0, 0.0, -1.0])
+    factor = 0.75
+    r = om.moe_forward(x, wr, b, k, lambda e: ex[e], E, "f32", lambda s: sh[s], 1,
+                       capacity_factor=factor)
+    L = x @ wr.T + b
+    P = scipy.special.softmax(L, axis=1)
+    sets = [sorted(max(itertools.combinations(range(E), k), key=lambda c: sum(L[t, list(c)])),
+                   key=lambda e: -L[t, e]) for t in range(T)]
+    idx = np.array(sets)
+    keep = _keep_by_sort(idx, E, math.ceil(T * k / E * factor))
+    assert (~keep).sum() > 0
+    assert np.array_equal(r.keep, keep)
+    y = np.zeros((T, d))
+    for t in range(T):
+        g = P[t, idx[t]] / P[t, idx[t]].sum()
+        for j in range(k):
+            if keep[t, j]:
+                y[t] += g[j] * torch_ffn(x[t], *ex[idx[t, j]])[0]
+        y[t] += torch_ffn(x[t], *sh[0])[0]
+    assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
+
+
+def check_sigmoid_layer_bruteforce(seed=26, T=20, d=12, E=5, k=2, f=16):
+    """The whole layer with sigmoid scoring against a dense evaluation."""
+    x, wr, b, ex, sh = rand_layer(seed, T, d, E, k, f)
+    r = om.moe_forward(x, wr, b, k, lambda e: ex[e], E, "f32", scoring="sigmoid")
+    s = scipy.special.expit(x @ wr.T)
+    y = np.zeros((T, d))
+    for t in range(T):
+        key = s[t] + b
+        best = list(max(itertools.combinations(range(E), k), key=lambda c: sum(key[list(c)])))
+        gate = np.zeros(E)
+        gate[best] = s[t, best] / s[t, best].sum()
+        for e in range(E):
+            y[t] += gate[e] * torch_ffn(x[t], *ex[e])[0]
+    assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
+
+
 ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, check_tie_break,
        check_softmax_library, check_invariants, check_uniform_gates,
        check_single_expert_library, check_silu, check_widen, check_occupancy_table,
-       check_occupancy_monte_carlo]
+       check_occupancy_monte_carlo, check_sigmoid_library, check_sigmoid_bias_selection_only,
+       check_sigmoid_routing_bruteforce, check_raw_softmax_weights, check_capacity_closed_forms,
+       check_capacity_bruteforce, check_sigmoid_layer_bruteforce]

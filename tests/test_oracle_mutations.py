@@ -50,7 +50,43 @@ def _unstable_order(idx, E):
     return np.argsort(np.asarray(idx).ravel(), kind="quicksort")[::-1].astype(np.int64)
 
 
+def _sigmoid_of_biased_logit(L, Pm, bias, scoring):
+    if scoring == "sigmoid" and bias is not None:
+        return om.sigmoid(L + np.asarray(bias)[None, :])
+    return L if scoring == "softmax" else Pm
+
+
+def _sign_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(z))
+
+
+def _keep_last(idx, E, capacity):
+    idx = np.asarray(idx)
+    flat = idx.ravel()[::-1]
+    taken = np.zeros(E, dtype=np.int64)
+    keep = np.zeros(flat.shape, dtype=bool)
+    for p, e in enumerate(flat.tolist()):
+        keep[p] = taken[e] < capacity
+        taken[e] += 1
+    return keep[::-1].reshape(idx.shape)
+
+
+def _capacity_floor(T, k, E, factor):
+    return int(T * k / E * factor)
+
+
+def _capacity_per_token(T, k, E, factor):
+    return int(np.ceil(T / E * factor))
+
+
 MUTANTS = [
+    ("selection_keys", _sigmoid_of_biased_logit, P.check_sigmoid_bias_selection_only),
+    ("sigmoid", _sign_sigmoid, P.check_sigmoid_library),
+    ("sigmoid", _sign_sigmoid, P.check_sigmoid_routing_bruteforce),
+    ("capacity_keep", _keep_last, P.check_capacity_bruteforce),
+    ("expert_capacity", _capacity_floor, P.check_capacity_closed_forms),
+    ("expert_capacity", _capacity_per_token, P.check_capacity_closed_forms),
+    ("kept_scores", lambda Pm, idx: om.renormalise(Pm, idx), P.check_raw_softmax_weights),
     ("select_topk", _ties_to_high, P.check_tie_break),
     ("select_topk", _ascending, P.check_worked_example_routing),
     ("renormalise", _no_renorm, P.check_invariants),
