@@ -17,8 +17,30 @@
  * Tokens are grouped by expert before the expert multiplies (page "Mixture of
  * experts: how MoE works and what it costs", section "What mixture of experts
  * costs in compute"; page "Mixture of Experts: why a model with 671 billion
- * parameters uses only 37", the router section's per-expert loop); every
- * (token, slot) pair is computed, none is dropped.
+ * parameters uses only 37", the router section's per-expert loop); by
+ * default every (token, slot) pair is computed, none is dropped.
+ *
+ * Router options of the descriptor (the defaults, all zero, give the layer
+ * above):
+ *  - scoring = MOE_SCORING_SIGMOID (page "Mixture of Experts: why a model
+ *    with 671 billion parameters uses only 37", sections "How many experts to
+ *    pick and how to score them: top-k, softmax, sigmoid" and "The problem
+ *    learned routing brings: load balancing"; page "Mixture of experts: how
+ *    MoE works and what it costs", "Why load balancing is the hard part of
+ *    MoE"): s[t,e] = sigmoid(x[t] . w_router[e]) per expert; the router bias
+ *    only steers the choice, idx = the k largest s[t,e] + router_bias[e]
+ *    (ties -> lower e), and w[t,j] = s[t,idx[t,j]] / sum_j' s[t,idx[t,j']].
+ *  - weighting = MOE_WEIGHTS_RAW (page "Mixture of Experts Explained...",
+ *    "Why top-1 routing cannot renormalise"): w[t,j] is the kept score as it
+ *    is, p[t,idx[t,j]] (softmax over all E) or s[t,idx[t,j]], not divided by
+ *    the kept sum.
+ *  - capacity_factor > 0 (page "Mixture of Experts: why a model with 671
+ *    billion parameters uses only 37", "Capacity factor: when tokens don't
+ *    fit"; page "Mixture of Experts Explained...", the capacity passage in
+ *    "Noise and the second expert"): each expert takes at most
+ *    C = ceil(T*k/E * capacity_factor) pairs (evaluated in that order in IEEE
+ *    double), the first C that chose it in pair order t*k+j.  A later pair is
+ *    dropped: its term is missing from y and its slot_row is -1.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
@@ -48,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -65,6 +87,12 @@ typedef enum moe_status {
  * always use their float32 kernels. */
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2 } moe_path;
 
+/* Router scores (see the options above). */
+typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } moe_scoring;
+
+/* Routing weights: kept scores renormalised over the kept set, or raw. */
+typedef enum moe_weighting { MOE_WEIGHTS_RENORM = 0, MOE_WEIGHTS_RAW = 1 } moe_weighting;
+
 typedef struct moe_desc {
   int64_t T;          /* tokens, >= 0                                        */
   int32_t d;          /* hidden size                                         */
@@ -76,7 +104,10 @@ typedef struct moe_desc {
   int32_t dtype;      /* moe_dtype of x and all weights                      */
   int32_t y_dtype;    /* moe_dtype of y                                      */
   int32_t path;       /* moe_path                                            */
+  int32_t scoring;    /* moe_scoring                                         */
+  int32_t weighting;  /* moe_weighting                                       */
   int32_t flags;      /* reserved, must be 0                                 */
+  double capacity_factor; /* 0: dropless; > 0: expert capacity (see above)   */
 } moe_desc;
 
 /* Stream handle: a hipStream_t passed as an opaque pointer. */
@@ -90,7 +121,8 @@ const char* moe_status_str(int status);
 
 /* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG (T<0, d/E/k/
  * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
- * n_shared > 0, bad enum, flags != 0, T*(k+n_shared) >= 2^31) or
+ * n_shared > 0, bad enum, flags != 0, capacity_factor negative or not finite,
+ * T*(k+n_shared) >= 2^31) or
  * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
  * 64, or with x (T*d), h ((T*(k+n_shared)+256)*max ffn) or one expert's
  * weight matrix (max ffn * d) reaching 4 GiB, as the bf16 kernels address
@@ -121,7 +153,8 @@ int64_t moe_grouped_rows(const moe_desc* desc);
  *   y            [T,d]            y_dtype (output)
  *   topk_idx     [T,k] int32      optional output (NULL: kept in workspace)
  *   topk_w       [T,k] float32    optional output
- *   expert_counts [E] int32       optional output: (token, slot) pairs per expert
+ *   expert_counts [E] int32       optional output: (token, slot) pairs routed to
+ *                                 each expert (before any capacity cut)
  *   workspace    >= moe_workspace_size(desc) bytes, 256-byte aligned
  */
 int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
@@ -148,8 +181,9 @@ int moe_forward_timed(const moe_desc* desc, const void* x, const void* w_router,
 /*
  * Step 1-3: router logits, softmax, top-k and renormalisation (page "Mixture
  * of Experts Explained...", steps Score, Normalise, Keep the top k,
- * Renormalise).  Logits are accumulated in float32; selection compares float32
- * logits, ties to the lower index.
+ * Renormalise), or the scoring / weighting options of the descriptor.
+ * Logits are accumulated in float32; selection compares float32 keys (the
+ * logits, or sigmoid scores plus bias), ties to the lower index.
  *   topk_idx [T,k] int32 (required), topk_w [T,k] float32 (required).
  */
 int moe_route(const moe_desc* desc, const void* x, const void* w_router,
@@ -162,11 +196,15 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  *   expert_counts [E]        pairs routed to each expert
  *   group_offsets [E+n_shared+1]  first grouped row of each group: routed
  *                 experts 0..E-1 in order, then shared experts; the last entry
- *                 is the row count T*(k+n_shared)
+ *                 is the row count, T*(k+n_shared) less any dropped pairs
  *   sorted_token  [T*(k+n_shared)] token of each grouped row; within a routed
  *                 group rows follow increasing t*k+j (a stable grouping);
- *                 shared group s holds tokens 0..T-1 in order
- *   slot_row      [T,k]      grouped row of pair (t,j)
+ *                 shared group s holds tokens 0..T-1 in order; entries past
+ *                 the row count are not written
+ *   slot_row      [T,k]      grouped row of pair (t,j), or -1 when a capacity
+ *                 cut dropped the pair
+ * With a capacity factor, expert e's group holds min(expert_counts[e], C)
+ * rows.
  */
 int moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* expert_counts,
                  int32_t* group_offsets, int32_t* sorted_token, int32_t* slot_row,
@@ -189,7 +227,8 @@ int moe_experts(const moe_desc* desc, const void* x, const void* w_up, const voi
  * and combine; page "Mixture of Experts (MoE)...", "Shared experts"):
  *   y[t,:] = sum_{j<k} topk_w[t,j] * expert_out[slot_row[t,j],:]
  *            + sum_s expert_out[group_offsets[E+s] + t, :]
- * summed in that order, in float32, then stored as y_dtype.
+ * summed in that order, in float32, then stored as y_dtype.  A pair with
+ * slot_row -1 (dropped) adds nothing.
  */
 int moe_combine(const moe_desc* desc, const float* expert_out, const float* topk_w,
                 const int32_t* slot_row, const int32_t* group_offsets, void* y,

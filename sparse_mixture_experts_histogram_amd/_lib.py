@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from ctypes import c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p, POINTER
+from ctypes import c_double, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p, POINTER
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
@@ -21,11 +21,17 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 
+SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
+WEIGHTS_RENORM, WEIGHTS_RAW = 0, 1
+ABI_VERSION = 2
+
+
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("E", c_int32), ("k", c_int32),
                 ("ffn", c_int32), ("n_shared", c_int32), ("ffn_shared", c_int32),
                 ("dtype", c_int32), ("y_dtype", c_int32), ("path", c_int32),
-                ("flags", c_int32)]
+                ("scoring", c_int32), ("weighting", c_int32), ("flags", c_int32),
+                ("capacity_factor", c_double)]
 
 
 class MoeError(RuntimeError):
@@ -58,6 +64,9 @@ def lib():
     D = POINTER(MoeDesc)
     L.moe_abi_version.restype = c_int
     L.moe_abi_version.argtypes = []
+    if L.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, the binding "
+                          f"expects {ABI_VERSION}; rebuild the library")
     L.moe_status_str.restype = c_char_p
     L.moe_status_str.argtypes = [c_int]
     L.moe_validate.restype = c_int

@@ -17,13 +17,28 @@ from ._lib import MoeDesc, MoeError
 
 _DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
 _PATHS = {"auto": _lib.PATH_AUTO, "prefill": _lib.PATH_PREFILL, "decode": _lib.PATH_DECODE}
+_SCORING = {"softmax": _lib.SCORING_SOFTMAX, "sigmoid": _lib.SCORING_SIGMOID}
+
+
+@dataclass(frozen=True)
+class Routing:
+    """Router options: ``scoring`` "softmax" (default) or "sigmoid" (the bias
+    then steers selection only); ``renormalize`` False keeps the raw kept
+    scores; ``capacity_factor`` > 0 caps each expert at
+    ceil(T*k/E*capacity_factor) pairs (0: dropless)."""
+    scoring: str = "softmax"
+    renormalize: bool = True
+    capacity_factor: float = 0.0
 
 
 def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
-              dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto") -> MoeDesc:
+              dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto",
+              routing: Routing = Routing()) -> MoeDesc:
     return MoeDesc(T=T, d=d, E=E, k=k, ffn=ffn, n_shared=n_shared,
                    ffn_shared=ffn_shared if n_shared else 0, dtype=_DT[dtype],
-                   y_dtype=_DT[y_dtype], path=_PATHS[path], flags=0)
+                   y_dtype=_DT[y_dtype], path=_PATHS[path], scoring=_SCORING[routing.scoring],
+                   weighting=_lib.WEIGHTS_RENORM if routing.renormalize else _lib.WEIGHTS_RAW,
+                   flags=0, capacity_factor=float(routing.capacity_factor))
 
 
 def _check(status: int, where: str):
@@ -86,11 +101,12 @@ class Weights:
     ws_gate: Optional[torch.Tensor] = None
     ws_down: Optional[torch.Tensor] = None  # [S, d, ffn_s]
 
-    def desc(self, T: int, k: int, y_dtype=torch.float32, path: str = "auto") -> MoeDesc:
+    def desc(self, T: int, k: int, y_dtype=torch.float32, path: str = "auto",
+             routing: Routing = Routing()) -> MoeDesc:
         E, ffn, d = self.w_up.shape
         ns = 0 if self.ws_up is None else self.ws_up.shape[0]
         fs = 0 if self.ws_up is None else self.ws_up.shape[1]
-        return make_desc(T, d, E, k, ffn, ns, fs, self.w_up.dtype, y_dtype, path)
+        return make_desc(T, d, E, k, ffn, ns, fs, self.w_up.dtype, y_dtype, path, routing)
 
 
 def _check_weights(W: Weights, x: torch.Tensor):
@@ -110,11 +126,12 @@ def _check_weights(W: Weights, x: torch.Tensor):
 
 
 def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path: str = "auto",
-                ws: Optional[torch.Tensor] = None, return_routing: bool = False):
+                ws: Optional[torch.Tensor] = None, return_routing: bool = False,
+                routing: Routing = Routing()):
     """y = MoE(x).  With return_routing, also (topk_idx, topk_w, expert_counts)."""
     _check_weights(W, x)
     T = x.shape[0]
-    desc = W.desc(T, k, y_dtype, path)
+    desc = W.desc(T, k, y_dtype, path, routing)
     dev = x.device
     if ws is None:
         ws = workspace(desc, dev)
@@ -134,11 +151,12 @@ def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path
 
 def moe_forward_timed(x: torch.Tensor, W: Weights, k: int, events, y: torch.Tensor,
                       ws: torch.Tensor, y_dtype=torch.float32, path: str = "auto",
-                      counts: Optional[torch.Tensor] = None) -> None:
+                      counts: Optional[torch.Tensor] = None,
+                      routing: Routing = Routing()) -> None:
     """moe_forward into preallocated y/ws, recording the 6 hipEvents at
     ``events`` (a void** from hipevents.Events.slice) around its launches."""
     T = x.shape[0]
-    desc = W.desc(T, k, y_dtype, path)
+    desc = W.desc(T, k, y_dtype, path, routing)
     st = _lib.lib().moe_forward_timed(ctypes.byref(desc), _ptr(x), _ptr(W.w_router),
                                       _ptr(W.bias), _ptr(W.w_up), _ptr(W.w_gate),
                                       _ptr(W.w_down), _ptr(W.ws_up), _ptr(W.ws_gate),
@@ -147,11 +165,12 @@ def moe_forward_timed(x: torch.Tensor, W: Weights, k: int, events, y: torch.Tens
     _check(st, "moe_forward_timed")
 
 
-def moe_route(x: torch.Tensor, W: Weights, k: int, ws: Optional[torch.Tensor] = None):
+def moe_route(x: torch.Tensor, W: Weights, k: int, ws: Optional[torch.Tensor] = None,
+              routing: Routing = Routing()):
     """(topk_idx [T,k] int32, topk_w [T,k] float32)."""
     _check_weights(W, x)
     T = x.shape[0]
-    desc = W.desc(T, k)
+    desc = W.desc(T, k, routing=routing)
     dev = x.device
     ws = workspace(desc, dev) if ws is None else ws
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)

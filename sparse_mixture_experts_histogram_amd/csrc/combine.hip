@@ -3,7 +3,8 @@
 // combine" of page "Mixture of Experts Explained: Routers, Active Parameters
 // and VRAM"; shared experts added with weight one per page "Mixture of Experts
 // (MoE): routing, expert parallelism, and memory", section "Shared
-// experts").  A gather per token, no atomics, so the result is deterministic.
+// experts").  A pair dropped by an expert capacity (slot_row -1) adds
+// nothing.  A gather per token, no atomics, so the result is deterministic.
 // When the down GEMM split K (into 2 to 4 ranges), each expert output row is
 // the sum of its partial rows, added here in range order.
 // HBM-bound: it reads (k + n_shared) float32 rows (per K range) and writes one
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int c = threadIdx.x; c < d4; c += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
+      if (rows[j] < 0) continue;  // pair dropped by an expert capacity
       const float4 v = row4(rows[j], c);
       const float wj = wts[j];
       acc.x = fmaf(wj, v.x, acc.x);

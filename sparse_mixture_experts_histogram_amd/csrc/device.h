@@ -82,6 +82,9 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Logistic sigmoid 1 / (1 + e^-z) with the library exponential.
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+
 // SiLU(g) * u with the hardware exponential and reciprocal (v_exp_f32,
 // v_rcp_f32: ~1 ulp each; the result is rounded to bf16 or compared at fp32
 // tolerance, far above that).

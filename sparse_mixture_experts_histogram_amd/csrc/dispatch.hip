@@ -5,10 +5,10 @@ namespace moe {
 
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
     const int32_t* __restrict__ idx, int32_t* blk_hist, const int32_t* __restrict__ blk_rank,
-    int T, int k, int E, int n_sh, int nblk, int32_t* counts, int32_t* offsets,
+    int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
     int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
     TileCfg cd) {
-  dispatch_body(idx, blk_hist, blk_rank, T, k, E, n_sh, nblk, counts, offsets, sorted_token,
+  dispatch_body(idx, blk_hist, blk_rank, T, k, E, n_sh, nblk, cap, counts, offsets, sorted_token,
                 slot_row, tiles_up, cu, tiles_down, cd);
 }
 
@@ -43,7 +43,7 @@ hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,
                            Tile* tiles_down, hipStream_t s) {
   const moe_desc& D = P.desc;
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispatchThreads), 0, s, idx, blk_hist,
-                     blk_rank, (int)D.T, D.k, D.E, D.n_shared, (int)P.nblk, counts, offsets,
+                     blk_rank, (int)D.T, D.k, D.E, D.n_shared, (int)P.nblk, P.cap, counts, offsets,
                      sorted_token, slot_row, tiles_up, tile_cfg(P.up), tiles_down,
                      tile_cfg(P.down));
   return hipGetLastError();

@@ -17,6 +17,11 @@
 //   3. writes the two GEMM tile schedules (see build_tiles);
 //   4. places each pair at offsets[e] + block_offset[b][e] + rank, which is a
 //      stable grouping (pairs of one expert keep increasing t*k+j order);
+//      with an expert capacity `cap` (page "Mixture of Experts: why a model
+//      with 671 billion parameters uses only 37", "Capacity factor: when
+//      tokens don't fit") a pair whose position in its expert's run,
+//      block_offset + rank, is cap or more is dropped (slot_row -1), and the
+//      expert's group holds min(count, cap) rows;
 //   5. fills the shared groups' rows with tokens 0..T-1.
 // Everything is integer work and deterministic.  The body is a device
 // function so that the router's finish kernel can run it when there is a
@@ -100,7 +105,7 @@ __device__ inline void build_tiles(const int* goff, const int* gsize, const int*
 // written idx, blk_hist and blk_rank through other pointers.)
 __device__ inline void dispatch_body(
     const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
-    int T, int k, int E, int n_sh, int nblk, int32_t* counts, int32_t* offsets,
+    int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
     int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
     TileCfg cd) {
   __shared__ int part[kDispatchThreads];
@@ -131,7 +136,7 @@ __device__ inline void dispatch_body(
       part[q * Ep + tid] = run;
       run += v;
     }
-    gsize[tid] = run;
+    gsize[tid] = min(run, cap);
     counts[tid] = run;
   }
   __syncthreads();
@@ -172,9 +177,13 @@ __device__ inline void dispatch_body(
     const int t = (int)(p / k);
     const int ee = idx[p];
     const int b = t / kRouterTokens;
-    const int row = goff[ee] + blk_hist[(int64_t)b * E + ee] + blk_rank[p];
-    slot_row[p] = row;
-    sorted_token[row] = t;
+    const int r = blk_hist[(int64_t)b * E + ee] + blk_rank[p];  // position in the expert's run
+    if (r < cap) {
+      slot_row[p] = goff[ee] + r;
+      sorted_token[goff[ee] + r] = t;
+    } else {
+      slot_row[p] = -1;
+    }
   }
   // 5. shared groups: identity rows
   for (int s = 0; s < n_sh; ++s)

@@ -2,6 +2,8 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
+#include <cmath>
 
 namespace moe {
 
@@ -38,7 +40,12 @@ static int validate(const moe_desc* d) {
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->y_dtype != MOE_F32 && d->y_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_DECODE) return MOE_ERR_INVALID_ARG;
+  if (d->scoring != MOE_SCORING_SOFTMAX && d->scoring != MOE_SCORING_SIGMOID)
+    return MOE_ERR_INVALID_ARG;
+  if (d->weighting != MOE_WEIGHTS_RENORM && d->weighting != MOE_WEIGHTS_RAW)
+    return MOE_ERR_INVALID_ARG;
   if (d->flags != 0) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(d->capacity_factor) || d->capacity_factor < 0) return MOE_ERR_INVALID_ARG;
   const int64_t rows = d->T * (int64_t)(d->k + d->n_shared);
   if (rows + kRowSlack >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARG;
   const int q = d->dtype == MOE_BF16 ? 64 : 4;
@@ -66,6 +73,15 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.pairs = T * d->k;
   P.R = T * (int64_t)(d->k + d->n_shared);
   P.nblk = cdiv(T, kRouterTokens);
+  P.route_mode = (d->scoring == MOE_SCORING_SIGMOID ? kRouteSigmoid : 0) |
+                 (d->weighting == MOE_WEIGHTS_RAW ? kRouteRaw : 0);
+  // Expert capacity ceil(T*k/E * factor), in IEEE double in that order; no
+  // expert receives more than T pairs, so larger capacities cut nothing.
+  P.cap = INT_MAX;
+  if (d->capacity_factor > 0) {
+    const double c = std::ceil((double)(T * d->k) / (double)d->E * d->capacity_factor);
+    P.cap = c < (double)T ? (int)c : INT_MAX;
+  }
   // With few token blocks the router's K range is split over up to
   // kMaxRouterSplit workgroups per block (at least four 32-wide k-steps
   // each), up to about 256 workgroups.

@@ -20,6 +20,8 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
 // Rows of slack after the grouped rows so tile loads past the end stay in bounds.
 constexpr int kRowSlack = 256;
+// Router option bits: sigmoid scores with a selection-only bias; raw weights.
+constexpr int kRouteSigmoid = 1, kRouteRaw = 2;
 
 // One GEMM tile: rows [m0, m_end) of group g, output columns [n0, n0 + BN).
 // Entry 0 of a schedule is a header: {entries, row tiles, column tiles, 0}.
@@ -50,6 +52,8 @@ struct Plan {
   int64_t pairs;     // T*k
   int64_t nblk;      // router blocks
   int rsplit;        // router workgroups per block (split K; 1 = one kernel)
+  int route_mode;    // kRouteSigmoid / kRouteRaw bits of the router options
+  int cap;           // expert capacity in pairs (INT_MAX: no cut)
   int ffn_max;       // max(ffn, ffn_shared)
   int kind;          // kernel family, see KernelKind
   GemmShape up, down;

@@ -18,6 +18,14 @@
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), which equals renormalising the
 // full softmax (page "Mixture of Experts Explained...", section "Softmax
 // before or after the top-k step").
+//
+// Router options (bits of `mode`): kRouteSigmoid ranks sigmoid(l) + bias and
+// weights the kept sigmoid(l) (the bias steers the choice only: page
+// "Mixture of Experts: why a model with 671 billion parameters uses only 37",
+// "How many experts to pick and how to score them"); kRouteRaw leaves the
+// kept scores unnormalised (page "Mixture of Experts Explained...", "Why
+// top-1 routing cannot renormalise"), so softmax weights then divide by the
+// sum over all E experts, one more pass over the token's logits.
 #include "device.h"
 #include "dispatch_body.h"
 #include "kernels.h"
@@ -43,24 +51,29 @@ __device__ void block_hist_rank(const int32_t* sel, int n_pairs, int E, int32_t*
 
 // Top-k of the tokens of one block from LDS logits lg[tl*ld + e].
 template <int EPL>
-__device__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int t0, int T,
-                           int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                           int32_t* sel) {
+__device__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int mode,
+                           int t0, int T, int E, int k, int32_t* __restrict__ idx_out,
+                           float* __restrict__ w_out, int32_t* sel) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const bool sig = mode & kRouteSigmoid, raw = mode & kRouteRaw;
   for (int tl = wave; tl < kRouterTokens; tl += nwaves) {
     const int t = t0 + tl;
     if (t >= T) break;
+    const float* lt = lg + tl * ld;
     uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
       if (e < E) {
-        const float v = lg[tl * ld + e] + (bias ? bias[e] : 0.0f);
+        const float b = bias ? bias[e] : 0.0f;
+        const float v = sig ? sigmoid_f32(lt[e]) + b : lt[e] + b;
         key[i] = ((uint64_t)order_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
       } else {
         key[i] = 0;
       }
     }
+    // kept score of slot j: exp(v_j - v_0) (softmax numerator relative to
+    // the largest key) or sigmoid(l_j)
     float v0 = 0.f, wsum = 0.f, my_w = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
@@ -74,43 +87,57 @@ __device__ void topk_block(const float* lg, int ld, const float* __restrict__ bi
       const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
       const float v = order_key_inv((uint32_t)(m >> 32));
       if (j == 0) v0 = v;
-      const float ex = expf(v - v0);
-      wsum += ex;
+      const float sc = sig ? sigmoid_f32(lt[e]) : expf(v - v0);
+      wsum += sc;
       if (lane == j) {
-        my_w = ex;
+        my_w = sc;
         my_e = e;
+      }
+    }
+    float denom = wsum;
+    if (raw) {
+      if (sig) {
+        denom = 1.0f;
+      } else {  // softmax over all E experts
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const int e = lane + 64 * i;
+          if (e < E) s += expf(lt[e] + (bias ? bias[e] : 0.0f) - v0);
+        }
+        denom = wave_sum_f32(s);
       }
     }
     if (lane < k) {
       idx_out[(int64_t)t * k + lane] = my_e;
-      w_out[(int64_t)t * k + lane] = my_w / wsum;
+      w_out[(int64_t)t * k + lane] = my_w / denom;
       sel[tl * k + lane] = my_e;
     }
   }
 }
 
 template <int EPL>
-__device__ void router_tail(float* lg, int ld, int32_t* sel, const float* bias, int t0, int T,
-                            int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
-                            int32_t* blk_rank) {
-  topk_block<EPL>(lg, ld, bias, t0, T, E, k, idx_out, w_out, sel);
+__device__ void router_tail(float* lg, int ld, int32_t* sel, const float* bias, int mode, int t0,
+                            int T, int E, int k, int32_t* idx_out, float* w_out,
+                            int32_t* blk_hist, int32_t* blk_rank) {
+  topk_block<EPL>(lg, ld, bias, mode, t0, T, E, k, idx_out, w_out, sel);
   __syncthreads();
   const int nt = min(kRouterTokens, T - t0);
   block_hist_rank(sel, nt * k, E, blk_hist + (int64_t)blockIdx.x * E,
                   blk_rank + (int64_t)t0 * k);
 }
 
-__device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const float* bias, int t0,
-                                     int T, int E, int k, int32_t* idx_out, float* w_out,
+__device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const float* bias, int mode,
+                                     int t0, int T, int E, int k, int32_t* idx_out, float* w_out,
                                      int32_t* blk_hist, int32_t* blk_rank) {
   if (E <= 64)
-    router_tail<1>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+    router_tail<1>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
   else if (E <= 128)
-    router_tail<2>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+    router_tail<2>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
   else if (E <= 256)
-    router_tail<4>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+    router_tail<4>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
   else
-    router_tail<8>(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+    router_tail<8>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
 }
 
 // Logits of the kRouterTokens tokens from t0 over k-steps [kb0, kb1) (32 k
@@ -188,14 +215,15 @@ __device__ void block_logits(const uint16_t* __restrict__ x, const uint16_t* __r
 template <int NT, int NW>
 __global__ __launch_bounds__(64 * NW) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int k, int KS, int32_t* idx_out,
-    float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
+    const float* __restrict__ bias, int mode, int T, int d, int E, int k, int KS,
+    int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank) {
   extern __shared__ float lds[];
   const int ld = ((E + 15) >> 4) * 16 + 4;
   int32_t* sel = (int32_t*)(lds + KS * kRouterTokens * ld);
   const int t0 = blockIdx.x * kRouterTokens;
   block_logits<NT, NW>(x, wr, T, d, E, KS, t0, 0, d >> 5, lds, ld);
-  router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  router_tail_dispatch(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist,
+                       blk_rank);
 }
 
 // Few token blocks: workgroup b computes the logits of token block
@@ -221,7 +249,7 @@ struct FusedDispatch {
   int32_t *counts, *offsets, *sorted_token, *slot_row;
   Tile *tiles_up, *tiles_down;
   TileCfg cu, cd;
-  int n_sh;
+  int n_sh, cap;
 };
 
 // Adds the nsplit (<= kMaxRouterSplit) partial logits of a token block in
@@ -235,7 +263,7 @@ struct FusedDispatch {
 // separate launch.)  kDispatchThreads threads; dynamic LDS: [16][ld] floats,
 // then sel[16*k].
 __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
-    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
+    const float* __restrict__ part, const float* __restrict__ bias, int mode, int T, int E, int k,
     int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank,
     FusedDispatch fd) {
   extern __shared__ float lds[];
@@ -255,16 +283,18 @@ __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     lds[(i / ep) * ld + i % ep] = s;
   }
   __syncthreads();
-  router_tail_dispatch(lds, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  router_tail_dispatch(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist,
+                       blk_rank);
   if (!fd.counts || nblk != 1) return;
   __syncthreads();  // the workgroup's own global writes are visible to it after the barrier
-  dispatch_body(idx_out, blk_hist, blk_rank, T, k, E, fd.n_sh, nblk, fd.counts, fd.offsets,
-                fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down, fd.cd);
+  dispatch_body(idx_out, blk_hist, blk_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts,
+                fd.offsets, fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down,
+                fd.cd);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    int T, int d, int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
+    int mode, int T, int d, int E, int k, int32_t* idx_out, float* w_out, int32_t* blk_hist,
     int32_t* blk_rank) {
   extern __shared__ float lds[];
   const int ld = E + 1;
@@ -289,7 +319,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     lg[tl * ld + e] = acc;
   }
   __syncthreads();
-  router_tail_dispatch(lg, ld, sel, bias, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  router_tail_dispatch(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
 }
 
 __global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restrict__ idx, int T,
@@ -312,8 +342,8 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
   if (D.dtype == MOE_F32) {
     const size_t lds = (size_t)kRouterTokens * (D.E + 1) * 4 + sel_bytes;
     hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), lds, s, (const float*)x,
-                       (const float*)w_router, bias, (int)D.T, D.d, D.E, D.k, idx, w, blk_hist,
-                       blk_rank);
+                       (const float*)w_router, bias, P.route_mode, (int)D.T, D.d, D.E, D.k, idx,
+                       w, blk_hist, blk_rank);
     return hipGetLastError();
   }
   // 4 waves; K is split over as many of them as the expert tiles leave free
@@ -336,7 +366,7 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
     if (dout && P.nblk == 1) {
       fd = FusedDispatch{dout->counts, dout->offsets, dout->sorted_token, dout->slot_row,
                          dout->tiles_up, dout->tiles_down, tile_cfg(P.up), tile_cfg(P.down),
-                         D.n_shared};
+                         D.n_shared, P.cap};
     }
     const dim3 pgrid((unsigned)(P.nblk * P.rsplit));
     auto partial = [&](auto kern) {
@@ -354,13 +384,13 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
-                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part, bias, (int)D.T, D.E,
-                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
+                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part, bias, P.route_mode,
+                       (int)D.T, D.E, D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
     return hipGetLastError();
   }
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, s, xb, wb, bias, (int)D.T, D.d, D.E, D.k,
-                       KS, idx, w, blk_hist, blk_rank);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, s, xb, wb, bias, P.route_mode, (int)D.T,
+                       D.d, D.E, D.k, KS, idx, w, blk_hist, blk_rank);
   };
   if (nt <= 1)
     args(router_bf16_kernel<1, NW>);

@@ -28,8 +28,9 @@ def bias_of(cfg: MoEConfig) -> Optional[np.ndarray]:
     return tables.router_bias(cfg)
 
 
-def margin_x(cfg: MoEConfig, T: int, w_r: np.ndarray, bias) -> np.ndarray:
-    """First T stream rows whose top-(k+1) logit gaps reach cfg.margin."""
+def margin_x(cfg: MoEConfig, T: int, w_r: np.ndarray, bias, scoring: str = "softmax") -> np.ndarray:
+    """First T stream rows whose top-(k+1) selection-key gaps reach cfg.margin
+    (keys: the logits, or sigmoid scores plus bias for sigmoid scoring)."""
     if T == 0:
         return generate.x_stream(cfg, 0)
     n = int(T * 1.2) + 32
@@ -37,11 +38,24 @@ def margin_x(cfg: MoEConfig, T: int, w_r: np.ndarray, bias) -> np.ndarray:
         xs = generate.x_stream(cfg, n)
         if cfg.margin <= 0:
             return xs[:T]
-        L = oracle.router_logits(oracle.widen(xs, cfg.dtype), oracle.widen(w_r, cfg.dtype), bias)
-        ok = np.nonzero(oracle.topk_gaps(L, cfg.k) >= cfg.margin)[0]
+        X, Wr = oracle.widen(xs, cfg.dtype), oracle.widen(w_r, cfg.dtype)
+        if scoring == "softmax":
+            K = oracle.router_logits(X, Wr, bias)
+        else:
+            L = oracle.router_logits(X, Wr, None)
+            K = oracle.selection_keys(L, oracle.sigmoid(L), bias, scoring)
+        ok = np.nonzero(oracle.topk_gaps(K, cfg.k) >= cfg.margin)[0]
         if len(ok) >= T:
             return np.ascontiguousarray(xs[ok[:T]])
         n *= 2
+
+
+@dataclass(frozen=True)
+class Options:
+    """Router options of a case (the oracle's arguments of the same names)."""
+    scoring: str = "softmax"
+    renormalize: bool = True
+    capacity_factor: Optional[float] = None
 
 
 @dataclass
@@ -56,6 +70,7 @@ class Case:
     s_up: Optional[np.ndarray] = None
     s_gate: Optional[np.ndarray] = None
     s_down: Optional[np.ndarray] = None
+    opts: Options = Options()
 
     def expert(self, e):
         return self.up[e], self.gate[e], self.down[e]
@@ -65,22 +80,27 @@ class Case:
 
     def oracle(self, tokens=None) -> "oracle.MoEResult":
         c = self.cfg
+        o = self.opts
         return oracle.moe_forward(self.x, self.w_router, self.bias, c.k, self.expert, c.E,
                                   c.dtype, self.shared if c.n_shared else None, c.n_shared,
-                                  tokens)
+                                  tokens, scoring=o.scoring, renormalize=o.renormalize,
+                                  capacity_factor=o.capacity_factor)
 
 
-def make_case(cfg: MoEConfig, T: Optional[int] = None) -> Case:
+def make_case(cfg: MoEConfig, T: Optional[int] = None, opts: Options = Options()) -> Case:
+    """Seeded layer of `cfg` with T tokens.  Named layers with the default
+    scoring read their kept rows from the stored tables; otherwise the rows
+    are filtered here by the margin on the scoring's selection keys."""
     T = cfg.T if T is None else T
     w_r = generate.router_weight(cfg)
     bias = bias_of(cfg)
-    if cfg.table is not None:
+    if cfg.table is not None and opts.scoring == "softmax":
         li = tables.layer_inputs(cfg, T)
         x = li.x
     else:
-        x = margin_x(cfg, T, w_r, bias)
+        x = margin_x(cfg, T, w_r, bias, opts.scoring)
     up, gate, down = generate.stacked_experts(cfg)
-    c = Case(cfg, x, w_r, bias, up, gate, down)
+    c = Case(cfg, x, w_r, bias, up, gate, down, opts=opts)
     if cfg.n_shared:
         c.s_up, c.s_gate, c.s_down = generate.stacked_experts(cfg, shared=True)
     return c

@@ -24,11 +24,12 @@ def test_exports_every_declared_symbol():
             "moe_workspace_size", "moe_validate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == _lib.ABI_VERSION == 2
 
 
 def test_desc_struct_size():
-    assert ctypes.sizeof(_lib.MoeDesc) == 48
+    assert ctypes.sizeof(_lib.MoeDesc) == 64
+    assert _lib.MoeDesc.capacity_factor.offset == 56
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -46,6 +47,14 @@ def test_desc_struct_size():
     (dict(y_dtype=5), INVALID),
     (dict(path=3), INVALID),
     (dict(flags=1), INVALID),
+    (dict(scoring=1), OK),
+    (dict(scoring=2), INVALID),
+    (dict(weighting=1), OK),
+    (dict(weighting=-1), INVALID),
+    (dict(capacity_factor=1.25), OK),
+    (dict(capacity_factor=-0.5), INVALID),
+    (dict(capacity_factor=float("nan")), INVALID),
+    (dict(capacity_factor=float("inf")), INVALID),
     (dict(T=2 ** 30, k=2), INVALID),
     (dict(d=96), UNSUPPORTED),
     (dict(ffn=100), UNSUPPORTED),
