@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle runs (median taken)")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the router options: sigmoid / raw routing on the "
+                         "DeepSeek-V3-shaped router and capacity cuts on the Mixtral-shaped "
+                         "layer (reported under \"variants\")")
     return ap.parse_args()
 
 
@@ -168,6 +172,72 @@ def decode_leg(cfg, x, W, k, iters):
     return dec
 
 
+def time_variants(cfg, x, W, k, steps):
+    """Router options, timed with events on the launch stream (mean of
+    `steps` calls after 5 warm-up calls each):
+
+    * moe_route on the DeepSeek-V3-shaped router (T=4096, d=7168, E=256,
+      top-8, bias ~ N(0, 0.5)) with softmax, sigmoid and raw-weight scoring;
+      bytes are x and W_r read once plus the indices and weights written;
+    * the whole Mixtral-shaped T=4096 layer with capacity factors 1.0 and
+      1.25 (the dropless layer is the headline), with the dropped pairs."""
+    import numpy as np
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from moe_inputs import NAMED, generate, tables
+
+    def ev_time(fn):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    out = {}
+    ds = NAMED["deepseek_v3"]
+    T = 4096
+    li = tables.layer_inputs(ds, T)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    xd = bf(li.x)
+    # expert weights are not read by the router: uninitialised storage of the right shape
+    Wd = moe.Weights(w_router=bf(generate.router_weight(ds)),
+                     w_up=torch.empty((ds.E, ds.ffn, ds.d), dtype=torch.bfloat16, device="cuda"),
+                     w_gate=torch.empty((ds.E, ds.ffn, ds.d), dtype=torch.bfloat16, device="cuda"),
+                     w_down=torch.empty((ds.E, ds.d, ds.ffn), dtype=torch.bfloat16, device="cuda"),
+                     bias=torch.from_numpy(generate.normal_bias(ds)).cuda())
+    ws = moe.workspace(Wd.desc(T, ds.k), xd.device)
+    rbytes = T * ds.d * 2 + ds.E * ds.d * 2 + T * ds.k * 8
+    router = {}
+    for name, rt in (("softmax", moe.Routing()), ("sigmoid", moe.Routing(scoring="sigmoid")),
+                     ("sigmoid_raw", moe.Routing(scoring="sigmoid", renormalize=False)),
+                     ("softmax_raw", moe.Routing(renormalize=False))):
+        ms = ev_time(lambda: moe.moe_route(xd, Wd, ds.k, ws=ws, routing=rt))
+        router[name] = {"us": round(ms * 1e3, 2),
+                        "hbm_frac": round(rbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+    out["router_deepseek_v3_t4096"] = {"algorithmic_bytes": rbytes, **router}
+    del xd, Wd, ws
+    torch.cuda.empty_cache()
+
+    Tm = x.shape[0]
+    cap_out = {}
+    for f in (1.0, 1.25):
+        rt = moe.Routing(capacity_factor=f)
+        wsm = moe.workspace(W.desc(Tm, k, routing=rt), x.device)
+        ms = ev_time(lambda: moe.moe_forward(x, W, k, ws=wsm, routing=rt))
+        _, _, _, counts = moe.moe_forward(x, W, k, ws=wsm, routing=rt, return_routing=True)
+        cnt = counts.cpu().numpy()
+        cap = int(np.ceil(Tm * k / cfg.E * f))
+        cap_out[str(f)] = {"ms": round(ms, 4), "tokens_per_s": round(Tm / ms * 1e3, 1),
+                           "capacity": cap, "dropped_pairs": int(np.clip(cnt - cap, 0, None).sum())}
+        del wsm
+    out["capacity_mixtral_t4096"] = cap_out
+    return out
+
+
 def kernel_source_hash() -> str:
     """Hash of the expert-GEMM kernel source the library was built from."""
     import hashlib
@@ -264,6 +334,11 @@ def main():
         dec = decode_leg(cfg, x, W, k, args.decode_iters)
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
 
+    variants = None
+    if args.variants:
+        variants = time_variants(cfg, x, W, k, args.steps)
+        print(f"[bench] variants: {variants}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, li, args.cpu_sample, args.cpu_reps)
@@ -289,6 +364,7 @@ def main():
         "expert_counts": [int(c) for c in counts],
         "decode": dec,
         "cpu_baseline": cpu,
+        **({"variants": variants} if variants is not None else {}),
         "host": {"cpu": platform.processor() or platform.machine(),
                  "cores_visible": len(os.sched_getaffinity(0))},
     }
