@@ -50,8 +50,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle runs (median taken)")
     ap.add_argument("--variants", action="store_true",
                     help="also time the router options: sigmoid / raw routing on the "
-                         "DeepSeek-V3-shaped router and capacity cuts on the Mixtral-shaped "
-                         "layer (reported under \"variants\")")
+                         "DeepSeek-V3-shaped router, capacity cuts on the Mixtral-shaped "
+                         "layer, and MXFP4 experts on the gpt-oss-shaped decode layer "
+                         "(reported under \"variants\")")
     return ap.parse_args()
 
 
@@ -180,7 +181,8 @@ def time_variants(cfg, x, W, k, steps):
       top-8, bias ~ N(0, 0.5)) with softmax, sigmoid and raw-weight scoring;
       bytes are x and W_r read once plus the indices and weights written;
     * the whole Mixtral-shaped T=4096 layer with capacity factors 1.0 and
-      1.25 (the dropless layer is the headline), with the dropped pairs."""
+      1.25 (the dropless layer is the headline), with the dropped pairs;
+    * the gpt-oss-shaped layer with MXFP4 experts at decode batch sizes."""
     import numpy as np
     import torch
     import sparse_mixture_experts_histogram_amd as moe
@@ -235,7 +237,59 @@ def time_variants(cfg, x, W, k, steps):
                            "capacity": cap, "dropped_pairs": int(np.clip(cnt - cap, 0, None).sum())}
         del wsm
     out["capacity_mixtral_t4096"] = cap_out
+    out["mxfp4_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128], 50)
     return out
+
+
+def time_mx_decode(Ts, iters):
+    """The gpt-oss-shaped layer (d=2880, 128 experts, top-4, ffn 2880) with
+    MXFP4 expert weights at decode batch sizes: per-iteration hipEvents before
+    the first and after the last launch, L2 and MALL flushed by a 1 GiB read
+    between iterations, median of `iters`; HBM fraction on the touched
+    experts' code and scale bytes."""
+    import ctypes
+    import numpy as np
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from sparse_mixture_experts_histogram_amd.hipevents import Events
+    from moe_inputs import NAMED, generate, tables
+
+    cfg = NAMED["gpt_oss"]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    u, us, g, gs, dn, ds = generate.stacked_mxfp4(cfg)
+    li = tables.layer_inputs(cfg, max(Ts))
+    W = moe.MxWeights(w_router=torch.from_numpy(li.w_router.view(np.int16)).view(torch.bfloat16).cuda(),
+                      up=t(u), up_scale=t(us), gate=t(g), gate_scale=t(gs), down=t(dn),
+                      down_scale=t(ds))
+    del u, us, g, gs, dn, ds
+    xall = torch.from_numpy(li.x.view(np.int16)).view(torch.bfloat16).cuda()
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
+    per_expert = 3 * cfg.d * cfg.ffn * (0.5 + 1.0 / 32)
+    res = {}
+    for T in Ts:
+        x = xall[:T].contiguous()
+        ws = moe.workspace(W.desc(T, cfg.k), x.device)
+        y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+        ev = Events(6 * iters)
+        outer = [(ctypes.c_void_p * 6)(ev.ev[6 * i], None, None, None, None, ev.ev[6 * i + 5])
+                 for i in range(iters)]
+        for _ in range(5):
+            moe.moe_forward_mx(x, W, cfg.k, ws=ws, y=y)
+        for i in range(iters):
+            torch.sum(flush, dim=0, out=flush_sum)
+            moe.moe_forward_mx(x, W, cfg.k, ws=ws, y=y,
+                               events=ctypes.cast(outer[i], ctypes.c_void_p))
+        torch.cuda.synchronize()
+        ms = statistics.median(ev.ms(6 * i, 6 * i + 5) for i in range(iters))
+        ev.close()
+        _, _, _, counts = moe.moe_forward_mx(x, W, cfg.k, ws=ws, return_routing=True)
+        touched = int((counts > 0).sum())
+        res[str(T)] = {"ms": round(ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
+                       "experts_touched": touched,
+                       "hbm_frac": round(touched * per_expert / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+    del flush
+    return res
 
 
 def kernel_source_hash() -> str:

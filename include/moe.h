@@ -41,6 +41,16 @@
  *    C = ceil(T*k/E * capacity_factor) pairs (evaluated in that order in IEEE
  *    double), the first C that chose it in pair order t*k+j.  A later pair is
  *    dropped: its term is missing from y and its slot_row is -1.
+ *  - expert_format = MOE_EXPERTS_MXFP4 (page "Mixture of Experts: why a model
+ *    with 671 billion parameters uses only 37", "What to do about it in
+ *    practice"; page "Mixture of experts: how MoE works and what it costs",
+ *    "What mixture of experts costs in memory"): the routed and shared expert
+ *    weights are MXFP4 (the OCP Microscaling format: blocks of 32 elements
+ *    along K share an E8M0 scale 2^(S-127); elements are FP4 E2M1 codes, two
+ *    per byte, element 2i in the low nibble).  x, the router and y keep their
+ *    types; products use the exactly dequantised weights.  Such a layer is
+ *    run with moe_forward_mx, which also takes the scale arrays; it always
+ *    uses the streaming (decode) expert kernels, whatever `path` says.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
@@ -70,7 +80,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -93,6 +103,9 @@ typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } mo
 /* Routing weights: kept scores renormalised over the kept set, or raw. */
 typedef enum moe_weighting { MOE_WEIGHTS_RENORM = 0, MOE_WEIGHTS_RAW = 1 } moe_weighting;
 
+/* Storage of the expert weights: `dtype`, or MXFP4 (see the options above). */
+typedef enum moe_expert_format { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1 } moe_expert_format;
+
 typedef struct moe_desc {
   int64_t T;          /* tokens, >= 0                                        */
   int32_t d;          /* hidden size                                         */
@@ -106,6 +119,7 @@ typedef struct moe_desc {
   int32_t path;       /* moe_path                                            */
   int32_t scoring;    /* moe_scoring                                         */
   int32_t weighting;  /* moe_weighting                                       */
+  int32_t expert_format; /* moe_expert_format                                */
   int32_t flags;      /* reserved, must be 0                                 */
   double capacity_factor; /* 0: dropless; > 0: expert capacity (see above)   */
 } moe_desc;
@@ -122,7 +136,7 @@ const char* moe_status_str(int status);
 /* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG (T<0, d/E/k/
  * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
  * n_shared > 0, bad enum, flags != 0, capacity_factor negative or not finite,
- * T*(k+n_shared) >= 2^31) or
+ * MXFP4 experts with dtype MOE_F32, T*(k+n_shared) >= 2^31) or
  * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
  * 64, or with x (T*d), h ((T*(k+n_shared)+256)*max ffn) or one expert's
  * weight matrix (max ffn * d) reaching 4 GiB, as the bf16 kernels address
@@ -156,6 +170,7 @@ int64_t moe_grouped_rows(const moe_desc* desc);
  *   expert_counts [E] int32       optional output: (token, slot) pairs routed to
  *                                 each expert (before any capacity cut)
  *   workspace    >= moe_workspace_size(desc) bytes, 256-byte aligned
+ * A layer with MXFP4 experts needs moe_forward_mx (MOE_ERR_INVALID_ARG here).
  */
 int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 const float* router_bias, const void* w_up, const void* w_gate,
@@ -163,6 +178,33 @@ int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
                 int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                 moe_stream stream);
+
+/* Scale arrays of MXFP4 expert weights (uint8 E8M0, one per 32 elements
+ * along K): up, gate [E,ffn,d/32], down [E,d,ffn/32]; shared-expert
+ * counterparts [n_shared,...] or NULL when n_shared == 0. */
+typedef struct moe_mx_scales {
+  const void* up;
+  const void* gate;
+  const void* down;
+  const void* s_up;
+  const void* s_gate;
+  const void* s_down;
+} moe_mx_scales;
+
+/*
+ * moe_forward for a layer with expert_format MOE_EXPERTS_MXFP4: w_up, w_gate
+ * [E,ffn,d/2], w_down [E,d,ffn/2] (and the shared counterparts) hold the
+ * packed E2M1 codes, `scales` their E8M0 scales.  Every other argument is as
+ * for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
+ * moe_forward_timed.  Scale bytes 0 (2^-127) and 255 (NaN) follow the format
+ * but results that leave bfloat16's normal range are not defined.
+ */
+int moe_forward_mx(const moe_desc* desc, const void* x, const void* w_router,
+                   const float* router_bias, const void* w_up, const void* w_gate,
+                   const void* w_down, const void* ws_up, const void* ws_gate,
+                   const void* ws_down, const moe_mx_scales* scales, void* y,
+                   int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
+                   size_t workspace_bytes, moe_stream stream, void* const* events);
 
 /*
  * moe_forward with timing marks: the same launches on the same stream, with
@@ -214,7 +256,8 @@ int moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* expert_
  * Steps 5-6: grouped expert FFNs over the grouped rows (SwiGLU up/gate, then
  * down).  For grouped row r of group g with token t = sorted_token[r]:
  *   expert_out[r,:] = FFN_g(x[t,:])       float32 [T*(k+n_shared), d]
- * group_offsets / sorted_token as produced by moe_dispatch.
+ * group_offsets / sorted_token as produced by moe_dispatch.  Dense expert
+ * weights only (MOE_ERR_INVALID_ARG for MXFP4).
  */
 int moe_experts(const moe_desc* desc, const void* x, const void* w_up, const void* w_gate,
                 const void* w_down, const void* ws_up, const void* ws_gate,

@@ -18,7 +18,13 @@ Recipe (all draws are numpy PCG64 streams keyed by
 * per routed expert e: W_up, W_gate [ffn, d] ~ N(0, 1/d), W_down [d, ffn]
   ~ N(0, 1/ffn); shared experts likewise with ffn_shared;
 * router bias: 'normal' draws float64 N(0, 1) times sqrt(bias_var), stored as
-  float32; 'zipf' is read from the stored table.
+  float32; 'zipf' is read from the stored table;
+* MXFP4 expert weights (layers that store experts in that format): each
+  matrix draws its packed E2M1 code bytes uniformly (every code equally
+  likely) and one E8M0 scale byte per 32 elements along K, the byte
+  round(127 + log2(std / 2.9261)) plus a uniform draw from {-1, 0, 1};
+  2.9261 is the rms of the 16 equally likely E2M1 values, so the
+  weights' rms is within a factor of two of the dense recipe's std.
 """
 from __future__ import annotations
 
@@ -32,6 +38,10 @@ from .configs import MoEConfig
 
 # stream ids
 X, W_ROUTER, W_UP, W_GATE, W_DOWN, WS_UP, WS_GATE, WS_DOWN, BIAS = range(9)
+MX_UP, MX_GATE, MX_DOWN = range(9, 12)
+# rms of the E2M1 values when all 16 codes are equally likely: the values are
+# 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, sqrt(68.5 / 8)
+_E2M1_RMS = 2.9261
 
 
 def _rng(cfg: MoEConfig, tensor_id: int, expert_id: int = 0) -> np.random.Generator:
@@ -131,3 +141,43 @@ def stacked_experts(cfg: MoEConfig, shared: bool = False,
         up[e], gate[e], down[e] = u, g, dn
     return up, gate, down
 
+
+
+def _mx_draw(cfg: MoEConfig, tensor_id: int, expert_id: int, rows: int, cols: int,
+             std: float) -> Tuple[np.ndarray, np.ndarray]:
+    """(codes [rows, cols/2] uint8, scales [rows, cols/32] uint8) of one MXFP4
+    matrix whose values have an rms within a factor of two of ``std``."""
+    rng = _rng(cfg, tensor_id, expert_id)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    base = int(round(127 + np.log2(std / _E2M1_RMS)))
+    scales = (base + rng.integers(-1, 2, size=(rows, cols // 32))).astype(np.uint8)
+    return codes, scales
+
+
+def mxfp4_expert_weights(cfg: MoEConfig, e: int, shared: bool = False):
+    """((up codes, up scales), (gate codes, gate scales), (down codes, down
+    scales)) of routed expert e (or shared expert e) stored as MXFP4."""
+    f = cfg.ffn_shared if shared else cfg.ffn
+    sd_in, sd_mid = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(f)
+    ids = (MX_UP, MX_GATE, MX_DOWN)
+    sid = 1000 + e if shared else e
+    return (_mx_draw(cfg, ids[0], sid, f, cfg.d, sd_in),
+            _mx_draw(cfg, ids[1], sid, f, cfg.d, sd_in),
+            _mx_draw(cfg, ids[2], sid, cfg.d, f, sd_mid))
+
+
+def stacked_mxfp4(cfg: MoEConfig, shared: bool = False):
+    """All routed (or shared) MXFP4 experts stacked: (up, up_scale, gate,
+    gate_scale, down, down_scale) uint8 arrays."""
+    n = cfg.n_shared if shared else cfg.E
+    f = cfg.ffn_shared if shared else cfg.ffn
+    up = np.empty((n, f, cfg.d // 2), np.uint8)
+    up_s = np.empty((n, f, cfg.d // 32), np.uint8)
+    gate = np.empty_like(up)
+    gate_s = np.empty_like(up_s)
+    down = np.empty((n, cfg.d, f // 2), np.uint8)
+    down_s = np.empty((n, cfg.d, f // 32), np.uint8)
+    for e in range(n):
+        (up[e], up_s[e]), (gate[e], gate_s[e]), (down[e], down_s[e]) = \
+            mxfp4_expert_weights(cfg, e, shared)
+    return up, up_s, gate, gate_s, down, down_s

@@ -11,5 +11,6 @@ pages give for one MoE layer (see the docstrings of ``oracle.moe``).
 from .moe import (  # noqa: F401
     widen, router_logits, softmax, select_topk, renormalise, route, expert_counts,
     dispatch_order, silu, swiglu_expert, moe_forward, topk_gaps, share_touched,
-    sigmoid, kept_scores, selection_keys, expert_capacity, capacity_keep, MoEResult,
+    sigmoid, kept_scores, selection_keys, expert_capacity, capacity_keep, e2m1_value,
+    e8m0_value, dequant_mxfp4, widen_weight, MoEResult,
 )

@@ -50,6 +50,17 @@ Router variants (not the default layer; selected by arguments):
   its term is missing from y (the token would pass on through the residual
   connection, which this layer does not add).
 
+Low-bit expert weights (P2 "What to do about it in practice": experts take 4
+bits well, gpt-oss ships them in MXFP4; P3 "What mixture of experts costs in
+memory": MXFP4 expert weights; P4 "Why MoE models can feel fast anyway": 4
+bits per weight).  The pages name the format without defining it; the
+definition used is the OCP Microscaling (MX) format MXFP4: blocks of 32
+consecutive elements along K share one E8M0 scale 2^(S-127); each element is
+FP4 E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; exponent 0 is
+subnormal: 0 or 0.5).  Two elements per byte, element 2i in the low nibble.
+The layer computes with the dequantized weights exactly as with stored
+bf16/f32 weights.
+
 Parity status: every function here is pinned by a CPU test against the pages'
 printed worked example, closed forms, brute force or a library routine, except
 the Zipf bias calibration in ``make_input_tables.py``, whose outcome is an
@@ -74,6 +85,44 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code: (-1)^s * (e == 0 ? m/2 : 2^(e-1) * (1 + m/2))."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return -mag if s else mag
+
+
+def e8m0_value(byte: int) -> float:
+    """Value of an E8M0 scale byte: 2^(byte - 127); 255 is NaN."""
+    return float("nan") if byte == 255 else 2.0 ** (int(byte) - 127)
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 matrix -> float64.  codes [N, K/2] uint8 (element 2i in the low
+    nibble of byte i), scales [N, K/32] uint8 -> [N, K] = element * scale of
+    its 32-element block along K."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    N, half = codes.shape
+    K = 2 * half
+    if scales.shape != (N, K // 32) or K % 32:
+        raise ValueError("MXFP4 shapes")
+    table = np.array([e2m1_value(c) for c in range(16)])
+    el = np.empty((N, K), dtype=np.float64)
+    el[:, 0::2] = table[codes & 0xF]
+    el[:, 1::2] = table[codes >> 4]
+    sc = np.array([e8m0_value(b) for b in range(256)])[scales]
+    return (el.reshape(N, K // 32, 32) * sc[:, :, None]).reshape(N, K)
+
+
+def widen_weight(w, dtype: str) -> np.ndarray:
+    """A stored weight matrix -> float64: a bf16/f32 array, or for 'mxfp4'
+    a (codes, scales) pair."""
+    if dtype == "mxfp4":
+        return dequant_mxfp4(*w)
+    return widen(w, dtype)
 
 
 def router_logits(x: np.ndarray, w_router: np.ndarray,
@@ -247,7 +296,8 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
                 shared_fn: Optional[ExpertFn] = None, n_shared: int = 0,
                 tokens: Optional[Sequence[int]] = None, scoring: str = "softmax",
                 renormalize: bool = True,
-                capacity_factor: Optional[float] = None) -> MoEResult:
+                capacity_factor: Optional[float] = None,
+                expert_dtype: Optional[str] = None) -> MoEResult:
     """The whole layer (P4 step "Run and combine"; P1 "Shared experts"):
 
         y[t] = sum_{j<k} w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])
@@ -261,8 +311,11 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
     (default: all), so large layers can be checked on a sample.
     ``scoring`` / ``renormalize`` pick the router variant (see ``route``);
     with a ``capacity_factor`` the pairs beyond an expert's capacity (which
-    depends on every token's routing) add nothing to y.
+    depends on every token's routing) add nothing to y.  ``expert_dtype``
+    ('mxfp4') stores the expert weights (routed and shared) in another
+    format than x and the router (default: ``dtype``).
     """
+    edt = dtype if expert_dtype is None else expert_dtype
     X = widen(x, dtype)
     L, P, idx, w = route(X, widen(w_router, dtype), bias, k, scoring, renormalize)
     T = X.shape[0]
@@ -284,7 +337,7 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
         pairs = order[start:start + n_e]
         start += n_e
         rows = pairs // k
-        wu, wg, wd = (widen(a, dtype) for a in expert_fn(e))
+        wu, wg, wd = (widen_weight(a, edt) for a in expert_fn(e))
         out = swiglu_expert(X[tok[rows]], wu, wg, wd)
         slot_out[rows, pairs % k] = out
     y = np.zeros((len(tok), X.shape[1]))
@@ -293,6 +346,6 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
     for j in range(k):
         y += np.where(kt[:, j:j + 1], wt[:, j:j + 1] * slot_out[:, j], 0.0)
     for s in range(n_shared):
-        su, sg, sd = (widen(a, dtype) for a in shared_fn(s))
+        su, sg, sd = (widen_weight(a, edt) for a in shared_fn(s))
         y += swiglu_expert(X[tok], su, sg, sd)
     return MoEResult(y, idx, w, counts, L, P, tok, keep)

@@ -5,7 +5,8 @@ The layer runs in hand-written HIP kernels behind the C ABI of include/moe.h
 thin Python binding: PyTorch supplies device memory and the stream.
 """
 from .api import (  # noqa: F401
-    Routing, Weights, make_desc, moe_combine, moe_dispatch, moe_experts, moe_forward, moe_forward_timed,
+    MxWeights, Routing, Weights, make_desc, moe_combine, moe_dispatch, moe_experts, moe_forward,
+    moe_forward_mx, moe_forward_timed,
     moe_grouped_rows,
     moe_resolve_path, moe_route, moe_validate, moe_workspace_size, workspace,
 )

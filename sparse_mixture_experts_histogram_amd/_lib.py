@@ -23,15 +23,21 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 WEIGHTS_RENORM, WEIGHTS_RAW = 0, 1
-ABI_VERSION = 2
+EXPERTS_DENSE, EXPERTS_MXFP4 = 0, 1
+ABI_VERSION = 3
 
 
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("E", c_int32), ("k", c_int32),
                 ("ffn", c_int32), ("n_shared", c_int32), ("ffn_shared", c_int32),
                 ("dtype", c_int32), ("y_dtype", c_int32), ("path", c_int32),
-                ("scoring", c_int32), ("weighting", c_int32), ("flags", c_int32),
-                ("capacity_factor", c_double)]
+                ("scoring", c_int32), ("weighting", c_int32), ("expert_format", c_int32),
+                ("flags", c_int32), ("capacity_factor", c_double)]
+
+
+class MoeMxScales(ctypes.Structure):
+    _fields_ = [("up", c_void_p), ("gate", c_void_p), ("down", c_void_p),
+                ("s_up", c_void_p), ("s_gate", c_void_p), ("s_down", c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +86,9 @@ def lib():
     V = c_void_p
     L.moe_forward.restype = c_int
     L.moe_forward.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V]
+    L.moe_forward_mx.restype = c_int
+    L.moe_forward_mx.argtypes = [D, V, V, V, V, V, V, V, V, V, POINTER(MoeMxScales), V, V, V, V,
+                                 V, c_size_t, V, V]
     L.moe_forward_timed.restype = c_int
     L.moe_forward_timed.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V, V]
     L.moe_route.restype = c_int

@@ -33,11 +33,12 @@ class Routing:
 
 def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
               dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto",
-              routing: Routing = Routing()) -> MoeDesc:
+              routing: Routing = Routing(), mxfp4: bool = False) -> MoeDesc:
     return MoeDesc(T=T, d=d, E=E, k=k, ffn=ffn, n_shared=n_shared,
                    ffn_shared=ffn_shared if n_shared else 0, dtype=_DT[dtype],
                    y_dtype=_DT[y_dtype], path=_PATHS[path], scoring=_SCORING[routing.scoring],
                    weighting=_lib.WEIGHTS_RENORM if routing.renormalize else _lib.WEIGHTS_RAW,
+                   expert_format=_lib.EXPERTS_MXFP4 if mxfp4 else _lib.EXPERTS_DENSE,
                    flags=0, capacity_factor=float(routing.capacity_factor))
 
 
@@ -146,6 +147,84 @@ def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path
                                 _ptr(W.ws_gate), _ptr(W.ws_down), _ptr(y), _ptr(idx), _ptr(w),
                                 _ptr(counts), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "moe_forward")
+    return (y, idx, w, counts) if return_routing else y
+
+
+@dataclass
+class MxWeights:
+    """A layer whose expert weights are MXFP4: uint8 E2M1 code tensors
+    (two codes per byte, element 2i in the low nibble) and uint8 E8M0 scale
+    tensors (one per 32 elements along K).  Router weight (bf16) and bias as
+    in ``Weights``."""
+    w_router: torch.Tensor                 # [E, d] bf16
+    up: torch.Tensor                       # [E, ffn, d/2] uint8
+    up_scale: torch.Tensor                 # [E, ffn, d/32] uint8
+    gate: torch.Tensor
+    gate_scale: torch.Tensor
+    down: torch.Tensor                     # [E, d, ffn/2] uint8
+    down_scale: torch.Tensor               # [E, d, ffn/32] uint8
+    bias: Optional[torch.Tensor] = None    # [E] float32
+    s_up: Optional[torch.Tensor] = None    # shared experts, same layout with ffn_shared
+    s_up_scale: Optional[torch.Tensor] = None
+    s_gate: Optional[torch.Tensor] = None
+    s_gate_scale: Optional[torch.Tensor] = None
+    s_down: Optional[torch.Tensor] = None
+    s_down_scale: Optional[torch.Tensor] = None
+
+    def desc(self, T: int, k: int, y_dtype=torch.float32,
+             routing: Routing = Routing()) -> MoeDesc:
+        E, ffn, half_d = self.up.shape
+        ns = 0 if self.s_up is None else self.s_up.shape[0]
+        fs = 0 if self.s_up is None else self.s_up.shape[1]
+        return make_desc(T, 2 * half_d, E, k, ffn, ns, fs, torch.bfloat16, y_dtype, "auto",
+                         routing, mxfp4=True)
+
+
+def _check_mx(W: MxWeights, x: torch.Tensor):
+    E, ffn, half_d = W.up.shape
+    d = 2 * half_d
+    if x.dtype != torch.bfloat16 or W.w_router.dtype != torch.bfloat16:
+        raise ValueError("MXFP4 layers take bf16 x and router weight")
+    want = {"up": (E, ffn, d // 2), "gate": (E, ffn, d // 2), "down": (E, d, ffn // 2),
+            "up_scale": (E, ffn, d // 32), "gate_scale": (E, ffn, d // 32),
+            "down_scale": (E, d, ffn // 32)}
+    for name, shape in want.items():
+        t = getattr(W, name)
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be uint8 {shape}")
+    if tuple(W.w_router.shape) != (E, d) or x.shape[-1] != d:
+        raise ValueError("router weight or x does not match the experts")
+    if W.bias is not None and (W.bias.dtype != torch.float32 or tuple(W.bias.shape) != (E,)):
+        raise ValueError("bias must be float32 [E]")
+
+
+def moe_forward_mx(x: torch.Tensor, W: MxWeights, k: int, y_dtype=torch.float32,
+                   ws: Optional[torch.Tensor] = None, return_routing: bool = False,
+                   routing: Routing = Routing(), events=None, y: Optional[torch.Tensor] = None):
+    """y = MoE(x) with MXFP4 expert weights.  With return_routing, also
+    (topk_idx, topk_w, expert_counts).  ``events``: a void** of 6 hipEvents
+    (see moe_forward_timed) or None; ``y``: a preallocated output."""
+    _check_mx(W, x)
+    T = x.shape[0]
+    desc = W.desc(T, k, y_dtype, routing)
+    dev = x.device
+    if ws is None:
+        ws = workspace(desc, dev)
+    if y is None:
+        y = torch.empty((T, x.shape[1]), dtype=y_dtype, device=dev)
+    idx = w = counts = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((W.up.shape[0],), dtype=torch.int32, device=dev)
+    sc = _lib.MoeMxScales(_ptr(W.up_scale), _ptr(W.gate_scale), _ptr(W.down_scale),
+                          _ptr(W.s_up_scale), _ptr(W.s_gate_scale), _ptr(W.s_down_scale))
+    st = _lib.lib().moe_forward_mx(ctypes.byref(desc), _ptr(x), _ptr(W.w_router), _ptr(W.bias),
+                                   _ptr(W.up), _ptr(W.gate), _ptr(W.down), _ptr(W.s_up),
+                                   _ptr(W.s_gate), _ptr(W.s_down), ctypes.byref(sc), _ptr(y),
+                                   _ptr(idx), _ptr(w), _ptr(counts), _ptr(ws), ws.numel(),
+                                   _stream(dev), events)
+    _check(st, "moe_forward_mx")
     return (y, idx, w, counts) if return_routing else y
 
 

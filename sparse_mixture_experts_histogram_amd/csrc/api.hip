@@ -48,18 +48,22 @@ namespace {
 // moe_forward's launch sequence; events[i] (when non-null) is recorded on the
 // stream before launch i (router, dispatch, up/gate, down, combine) and
 // events[5] after the last one.
+// `mx` is the scale set of MXFP4 expert weights (null for dense weights).
 int forward_impl(const moe_desc* d, const void* x, const void* w_router,
                  const float* router_bias, const void* w_up, const void* w_gate,
                  const void* w_down, const void* ws_up, const void* ws_gate, const void* ws_down,
-                 void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
-                 void* workspace, size_t workspace_bytes, moe_stream stream,
-                 void* const* events) {
+                 const moe_mx_scales* mx, void* y, int32_t* topk_idx, float* topk_w,
+                 int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                 moe_stream stream, void* const* events) {
+  if (d && (d->expert_format == MOE_EXPERTS_MXFP4) != (mx != nullptr)) return MOE_ERR_INVALID_ARG;
   Plan P;
   bool empty = false;
   int st = prepare(d, workspace, workspace_bytes, &P, &empty);
   if (st != MOE_OK || empty) return st;
   if (!x || !w_router || !w_up || !w_gate || !w_down || !y) return MOE_ERR_INVALID_ARG;
   if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
+  if (mx && (!mx->up || !mx->gate || !mx->down || !shared_ok(d, mx->s_up, mx->s_gate, mx->s_down)))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) -> hipError_t {
     if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], s);
@@ -77,8 +81,13 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
   Tile* tu = W.at<Tile>(P.o_tiles_up);
   Tile* td = W.at<Tile>(P.o_tiles_down);
   float* out = W.at<float>(P.o_out);
+  MxScales sc{};
+  if (mx)
+    sc = MxScales{(const uint8_t*)mx->up,   (const uint8_t*)mx->gate,
+                  (const uint8_t*)mx->down, (const uint8_t*)mx->s_up,
+                  (const uint8_t*)mx->s_gate, (const uint8_t*)mx->s_down};
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
-               W.at<void>(P.o_h), out, P.down.ksplit};
+               W.at<void>(P.o_h), out, P.down.ksplit, sc};
   const int64_t part_stride = ((int64_t)P.R + kRowSlack) * d->d;
   // With a split router and one token block (at most 16 tokens) the router
   // also runs the dispatch, and events 1 and 2 mark the same point.
@@ -113,8 +122,20 @@ int moe_forward(const moe_desc* d, const void* x, const void* w_router, const fl
                 float* topk_w, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                 moe_stream stream) {
   return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
-                      ws_down, y, topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
-                      stream, nullptr);
+                      ws_down, nullptr, y, topk_idx, topk_w, expert_counts, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_mx(const moe_desc* d, const void* x, const void* w_router,
+                   const float* router_bias, const void* w_up, const void* w_gate,
+                   const void* w_down, const void* ws_up, const void* ws_gate,
+                   const void* ws_down, const moe_mx_scales* scales, void* y,
+                   int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
+                   size_t workspace_bytes, moe_stream stream, void* const* events) {
+  if (!scales) return MOE_ERR_INVALID_ARG;
+  return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
+                      ws_down, scales, y, topk_idx, topk_w, expert_counts, workspace,
+                      workspace_bytes, stream, events);
 }
 
 int moe_forward_timed(const moe_desc* d, const void* x, const void* w_router,
@@ -124,8 +145,8 @@ int moe_forward_timed(const moe_desc* d, const void* x, const void* w_router,
                       int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                       moe_stream stream, void* const* events) {
   return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
-                      ws_down, y, topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
-                      stream, events);
+                      ws_down, nullptr, y, topk_idx, topk_w, expert_counts, workspace,
+                      workspace_bytes, stream, events);
 }
 
 int moe_route(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
@@ -167,6 +188,7 @@ int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* 
                 const void* w_down, const void* ws_up, const void* ws_gate, const void* ws_down,
                 const int32_t* group_offsets, const int32_t* sorted_token, float* expert_out,
                 void* workspace, size_t workspace_bytes, moe_stream stream) {
+  if (d && d->expert_format != MOE_EXPERTS_DENSE) return MOE_ERR_INVALID_ARG;
   Plan P;
   bool empty = false;
   int st = prepare(d, workspace, workspace_bytes, &P, &empty);

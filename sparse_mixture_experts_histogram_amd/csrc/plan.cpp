@@ -14,17 +14,19 @@ namespace moe {
 static int prefill_rows(const moe_desc* d) {
   return d->T * d->k >= 384LL * d->E ? 256 : 128;
 }
+// The streaming kernels use 16-row tiles of 16 (bf16) or 32 (MXFP4) columns.
+static bool streaming(int kind) { return kind == KIND_BF16_DECODE || kind == KIND_MXFP4; }
 int up_row_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : streaming(kind) ? 16 : 32;
 }
 int up_col_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_BF16_DECODE ? 16 : 32;
+  return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_MXFP4 ? 32 : streaming(kind) ? 16 : 32;
 }
 int down_row_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : kind == KIND_BF16_DECODE ? 16 : 32;
+  return kind == KIND_BF16_PREFILL ? prefill_rows(d) : streaming(kind) ? 16 : 32;
 }
 int down_col_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_BF16_DECODE ? 16 : 32;
+  return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_MXFP4 ? 32 : streaming(kind) ? 16 : 32;
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -44,6 +46,9 @@ static int validate(const moe_desc* d) {
     return MOE_ERR_INVALID_ARG;
   if (d->weighting != MOE_WEIGHTS_RENORM && d->weighting != MOE_WEIGHTS_RAW)
     return MOE_ERR_INVALID_ARG;
+  if (d->expert_format != MOE_EXPERTS_DENSE && d->expert_format != MOE_EXPERTS_MXFP4)
+    return MOE_ERR_INVALID_ARG;
+  if (d->expert_format == MOE_EXPERTS_MXFP4 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->flags != 0) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d->capacity_factor) || d->capacity_factor < 0) return MOE_ERR_INVALID_ARG;
   const int64_t rows = d->T * (int64_t)(d->k + d->n_shared);
@@ -97,8 +102,11 @@ int make_plan(const moe_desc* d, Plan* p) {
     P.path = (T * d->k <= 8LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   else
     P.path = d->path;
+  if (d->expert_format == MOE_EXPERTS_MXFP4) P.path = MOE_PATH_DECODE;
   if (d->dtype == MOE_F32)
     P.kind = KIND_F32;
+  else if (d->expert_format == MOE_EXPERTS_MXFP4)
+    P.kind = KIND_MXFP4;
   else
     P.kind = P.path == MOE_PATH_DECODE ? KIND_BF16_DECODE : KIND_BF16_PREFILL;
 
@@ -117,7 +125,7 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.up = shape(up_row_tile(P.kind, d), up_col_tile(P.kind, d), d->ffn, d->ffn_shared);
   P.down = shape(down_row_tile(P.kind, d), down_col_tile(P.kind, d), d->d, d->d);
   // the decode kernels walk a compact list of row tiles (see dispatch.hip)
-  P.up.row_list = P.down.row_list = P.kind == KIND_BF16_DECODE;
+  P.up.row_list = P.down.row_list = streaming(P.kind);
   // Schedule order (measured on MI355X): both GEMMs run chunks of
   // consecutive entries per XCD; the up/gate GEMM with row tile fastest, the
   // down GEMM (long K, few column tiles) with column tile fastest.

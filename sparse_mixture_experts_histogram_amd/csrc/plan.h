@@ -62,7 +62,7 @@ struct Plan {
       o_slot, o_idx, o_w, o_h, o_out, total;
 };
 
-enum KernelKind { KIND_F32 = 0, KIND_BF16_PREFILL = 1, KIND_BF16_DECODE = 2 };
+enum KernelKind { KIND_F32 = 0, KIND_BF16_PREFILL = 1, KIND_BF16_DECODE = 2, KIND_MXFP4 = 3 };
 
 // Fill `p` for `d`; returns a moe_status.
 int make_plan(const moe_desc* d, Plan* p);

@@ -406,9 +406,76 @@ def check_sigmoid_layer_bruteforce(seed=26, T=20, d=12, E=5, k=2, f=16):
     assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
 
 
+# ---------------------------------------------------------------- MXFP4 expert weights
+def check_e2m1_table():
+    """The E2M1 element values of the OCP MX format: codes 0..7 are
+    0, 0.5, 1, 1.5, 2, 3, 4, 6 and codes 8..15 their negatives."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert om.e2m1_value(c) == mags[c]
+        assert om.e2m1_value(c + 8) == -mags[c]
+        assert math.copysign(1.0, om.e2m1_value(c + 8)) == -1.0
+
+
+def check_e8m0_library():
+    """E8M0 scale bytes against torch's float8_e8m0fnu conversion."""
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(torch.float8_e8m0fnu).float().double().numpy()
+    got = np.array([om.e8m0_value(int(v)) for v in range(256)])
+    assert np.array_equal(got[:255], ref[:255]) and np.isnan(got[255]) and np.isnan(ref[255])
+
+
+def _dequant_loop(codes, scales):
+    """Element by element: element k of row n is nibble k % 2 (low first) of
+    byte k // 2, times the scale of block k // 32."""
+    N, half = codes.shape
+    out = np.empty((N, 2 * half))
+    for n in range(N):
+        for k in range(2 * half):
+            code = (int(codes[n, k // 2]) >> (4 * (k % 2))) & 0xF
+            out[n, k] = om.e2m1_value(code) * 2.0 ** (int(scales[n, k // 32]) - 127)
+    return out
+
+
+def check_mxfp4_dequant(seed=27):
+    """Dequantisation against the element-by-element form, and a hand-made
+    row: byte 0x21 holds 0.5 (low nibble) then 1.0; the second block's scale
+    byte 129 multiplies it by 4."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(5, 48), dtype=np.uint8)
+    scales = rng.integers(110, 140, size=(5, 3), dtype=np.uint8)
+    assert np.array_equal(om.dequant_mxfp4(codes, scales), _dequant_loop(codes, scales))
+    row = np.full((1, 32), 0x21, dtype=np.uint8)
+    d = om.dequant_mxfp4(row, np.array([[127, 129]], dtype=np.uint8))[0]
+    assert d[:4].tolist() == [0.5, 1.0, 0.5, 1.0] and d[32:34].tolist() == [2.0, 4.0]
+
+
+def check_mxfp4_layer_bruteforce(seed=28, T=12, d=64, E=4, k=2, f=32):
+    """The layer with MXFP4 experts equals a dense evaluation on the
+    element-by-element dequantised weights."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / np.sqrt(d)
+    mx = [tuple((rng.integers(0, 256, size=(r, c // 2), dtype=np.uint8),
+                 rng.integers(120, 125, size=(r, c // 32), dtype=np.uint8))
+                for r, c in ((f, d), (f, d), (d, f))) for _ in range(E)]
+    r = om.moe_forward(x, wr, None, k, lambda e: mx[e], E, "f32", expert_dtype="mxfp4")
+    dense = [tuple(_dequant_loop(*m) for m in mx[e]) for e in range(E)]
+    P = scipy.special.softmax(x @ wr.T, axis=1)
+    y = np.zeros((T, d))
+    for t in range(T):
+        best = sorted(max(itertools.combinations(range(E), k),
+                          key=lambda c: sum((x @ wr.T)[t, list(c)])))
+        g = P[t, best] / P[t, best].sum()
+        for j, e in enumerate(best):
+            y[t] += g[j] * torch_ffn(x[t], *dense[e])[0]
+    assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
+
+
 ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, check_tie_break,
        check_softmax_library, check_invariants, check_uniform_gates,
        check_single_expert_library, check_silu, check_widen, check_occupancy_table,
        check_occupancy_monte_carlo, check_sigmoid_library, check_sigmoid_bias_selection_only,
        check_sigmoid_routing_bruteforce, check_raw_softmax_weights, check_capacity_closed_forms,
-       check_capacity_bruteforce, check_sigmoid_layer_bruteforce]
+       check_capacity_bruteforce, check_sigmoid_layer_bruteforce, check_e2m1_table,
+       check_e8m0_library, check_mxfp4_dequant, check_mxfp4_layer_bruteforce]

@@ -24,12 +24,13 @@ def test_exports_every_declared_symbol():
             "moe_workspace_size", "moe_validate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == _lib.ABI_VERSION == 2
+    assert L.moe_abi_version() == _lib.ABI_VERSION == 3
 
 
 def test_desc_struct_size():
-    assert ctypes.sizeof(_lib.MoeDesc) == 64
-    assert _lib.MoeDesc.capacity_factor.offset == 56
+    assert ctypes.sizeof(_lib.MoeDesc) == 72
+    assert _lib.MoeDesc.capacity_factor.offset == 64
+    assert ctypes.sizeof(_lib.MoeMxScales) == 48
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -55,6 +56,9 @@ def test_desc_struct_size():
     (dict(capacity_factor=-0.5), INVALID),
     (dict(capacity_factor=float("nan")), INVALID),
     (dict(capacity_factor=float("inf")), INVALID),
+    (dict(expert_format=1), OK),
+    (dict(expert_format=2), INVALID),
+    (dict(expert_format=1, dtype=0, d=64, ffn=64), INVALID),   # MXFP4 experts need bf16 x
     (dict(T=2 ** 30, k=2), INVALID),
     (dict(d=96), UNSUPPORTED),
     (dict(ffn=100), UNSUPPORTED),
@@ -86,6 +90,9 @@ def test_workspace_and_paths():
     assert moe.moe_resolve_path(desc(T=4096, d=7168, E=256, k=8, ffn=2048, n_shared=1,
                                      ffn_shared=2048)) == "prefill"
     assert moe.moe_grouped_rows(desc(T=10, k=3, n_shared=2, ffn_shared=64)) == 50
+    # MXFP4 experts always run the streaming kernels
+    assert moe.moe_resolve_path(desc(T=4096, d=4096, E=8, k=2, ffn=14336,
+                                     expert_format=1)) == "decode"
 
 
 def test_entry_points_reject_before_launch():

@@ -79,7 +79,38 @@ def _capacity_per_token(T, k, E, factor):
     return int(np.ceil(T / E * factor))
 
 
+def _e2m1_bias2(code):
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 2) * (1.0 + 0.5 * m)
+    return -mag if s else mag
+
+
+def _e8m0_bias128(byte):
+    return 2.0 ** (int(byte) - 128)
+
+
+def _dequant_high_nibble_first(codes, scales):
+    swapped = ((np.asarray(codes) & 0xF) << 4) | (np.asarray(codes) >> 4)
+    return _REAL_DEQUANT(swapped.astype(np.uint8), scales)
+
+
+def _dequant_block16(codes, scales):
+    codes = np.asarray(codes)
+    N, half = codes.shape
+    el = _REAL_DEQUANT(codes, np.full((N, 2 * half // 32), 127, np.uint8))
+    nb = np.asarray(scales).shape[1]
+    sc = 2.0 ** (np.asarray(scales, np.int64)[:, np.arange(2 * half // 16) % nb] - 127)
+    return (el.reshape(N, -1, 16) * sc[:, :, None]).reshape(N, -1)
+
+
+_REAL_DEQUANT = om.dequant_mxfp4
+
 MUTANTS = [
+    ("e2m1_value", _e2m1_bias2, P.check_e2m1_table),
+    ("e8m0_value", _e8m0_bias128, P.check_e8m0_library),
+    ("dequant_mxfp4", _dequant_high_nibble_first, P.check_mxfp4_dequant),
+    ("dequant_mxfp4", _dequant_block16, P.check_mxfp4_dequant),
+    ("dequant_mxfp4", _dequant_high_nibble_first, P.check_mxfp4_layer_bruteforce),
     ("selection_keys", _sigmoid_of_biased_logit, P.check_sigmoid_bias_selection_only),
     ("sigmoid", _sign_sigmoid, P.check_sigmoid_library),
     ("sigmoid", _sign_sigmoid, P.check_sigmoid_routing_bruteforce),
