@@ -123,9 +123,19 @@ __device__ inline void dispatch_body(
   const int S = kDispatchThreads / Ep;
   const int e = tid % Ep, seg = tid / Ep;
   const int b0 = (int)((int64_t)seg * nblk / S), b1 = (int)((int64_t)(seg + 1) * nblk / S);
+  // (Loads go in batches of kBatch independent loads: a thread walks up to
+  // nblk / S blocks, and one memory round trip per block was most of the
+  // dispatch time for many blocks and experts.)
+  constexpr int kBatch = 16;
   if (e < E) {
     int s = 0;
-    for (int b = b0; b < b1; ++b) s += blk_hist[(int64_t)b * E + e];
+    for (int b = b0; b < b1; b += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = b + i < b1 ? blk_hist[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) s += v[i];
+    }
     part[seg * Ep + e] = s;
   }
   __syncthreads();
@@ -142,11 +152,15 @@ __device__ inline void dispatch_body(
   __syncthreads();
   if (e < E) {
     int run = part[seg * Ep + e];
-    for (int b = b0; b < b1; ++b) {
-      const int64_t at = (int64_t)b * E + e;
-      const int v = blk_hist[at];
-      blk_hist[at] = run;
-      run += v;
+    for (int b = b0; b < b1; b += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = b + i < b1 ? blk_hist[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b + i < b1) blk_hist[(int64_t)(b + i) * E + e] = run;
+        run += v[i];
+      }
     }
   }
   if (tid >= E && tid < G) gsize[tid] = T;
@@ -171,18 +185,37 @@ __device__ inline void dispatch_body(
   build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up);
   build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down);
 
-  // 4. stable placement of the routed pairs
+  // 4. stable placement of the routed pairs, kPlace pairs per thread at a
+  // time (their index and rank loads, then their block-offset loads, are
+  // each one batch)
+  constexpr int kPlace = 8;
   const int64_t pairs = (int64_t)T * k;
-  for (int64_t p = tid; p < pairs; p += blockDim.x) {
-    const int t = (int)(p / k);
-    const int ee = idx[p];
-    const int b = t / kRouterTokens;
-    const int r = blk_hist[(int64_t)b * E + ee] + blk_rank[p];  // position in the expert's run
-    if (r < cap) {
-      slot_row[p] = goff[ee] + r;
-      sorted_token[goff[ee] + r] = t;
-    } else {
-      slot_row[p] = -1;
+  for (int64_t p0 = tid; p0 < pairs; p0 += (int64_t)kPlace * blockDim.x) {
+    int ee[kPlace], rk[kPlace], off[kPlace];
+#pragma unroll
+    for (int i = 0; i < kPlace; ++i) {
+      const int64_t p = p0 + (int64_t)i * blockDim.x;
+      ee[i] = p < pairs ? idx[p] : 0;
+      rk[i] = p < pairs ? blk_rank[p] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPlace; ++i) {
+      const int64_t p = p0 + (int64_t)i * blockDim.x;
+      const int b = (int)(p / k) / kRouterTokens;
+      off[i] = p < pairs ? blk_hist[(int64_t)b * E + ee[i]] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPlace; ++i) {
+      const int64_t p = p0 + (int64_t)i * blockDim.x;
+      if (p >= pairs) continue;
+      const int t = (int)(p / k);
+      const int r = off[i] + rk[i];  // position in the expert's run
+      if (r < cap) {
+        slot_row[p] = goff[ee[i]] + r;
+        sorted_token[goff[ee[i]] + r] = t;
+      } else {
+        slot_row[p] = -1;
+      }
     }
   }
   // 5. shared groups: identity rows

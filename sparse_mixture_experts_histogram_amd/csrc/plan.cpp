@@ -91,11 +91,22 @@ int make_plan(const moe_desc* d, Plan* p) {
   // kMaxRouterSplit workgroups per block (at least four 32-wide k-steps
   // each), up to about 256 workgroups.
   P.rsplit = 1;
+  P.rwide = 0;
   if (d->dtype == MOE_BF16) {
     const int64_t nk = d->d / 32;
-    while (P.rsplit < kMaxRouterSplit && P.nblk * P.rsplit * 2 <= 256 &&
-           nk / (P.rsplit * 2) >= 4)
-      P.rsplit *= 2;
+    if (kRouterWide > 0 && d->T >= 4 * kRouterWide && (int64_t)d->E * d->d >= kRouterWideMinWeights) {
+      // many tokens, large router matrix: 64-token workgroups over K parts,
+      // up to about 512 workgroups with at least 16 k-steps each
+      P.rwide = kRouterWide;
+      const int64_t groups = cdiv(d->T, kRouterWide);
+      while (P.rsplit < kMaxRouterSplit && groups * P.rsplit * 2 <= 512 &&
+             nk / (P.rsplit * 2) >= 16)
+        P.rsplit *= 2;
+    } else {
+      while (P.rsplit < kMaxRouterSplit && P.nblk * P.rsplit * 2 <= 256 &&
+             nk / (P.rsplit * 2) >= 4)
+        P.rsplit *= 2;
+    }
   }
   P.ffn_max = d->n_shared > 0 ? std::max(d->ffn, d->ffn_shared) : d->ffn;
   if (d->path == MOE_PATH_AUTO)
@@ -159,7 +170,9 @@ int make_plan(const moe_desc* d, Plan* p) {
   };
   const size_t rows_ws = (size_t)P.R + kRowSlack;
   const size_t e_pad = (size_t)(d->E + 15) / 16 * 16;
-  P.o_router_part = take(P.rsplit > 1 ? (size_t)P.rsplit * P.nblk * kRouterTokens * e_pad * 4 : 0);
+  const size_t part_rows =
+      P.rwide ? (size_t)cdiv(T, P.rwide) * P.rwide : (size_t)P.nblk * kRouterTokens;
+  P.o_router_part = take(P.rsplit > 1 || P.rwide ? (size_t)P.rsplit * part_rows * e_pad * 4 : 0);
   P.o_blk_hist = take((size_t)P.nblk * d->E * 4);
   P.o_blk_rank = take((size_t)P.pairs * 4);
   P.o_counts = take((size_t)d->E * 4);

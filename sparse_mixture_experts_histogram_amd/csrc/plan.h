@@ -14,6 +14,10 @@ namespace moe {
 constexpr int kRouterTokens = 16;
 // Most workgroups sharing one router block's K range.
 constexpr int kMaxRouterSplit = 16;
+// Wide router form (tokens per workgroup; 0 disables it), used from 4 such
+// groups of tokens and this many router weights (E * d) up.
+constexpr int kRouterWide = 64;
+constexpr int64_t kRouterWideMinWeights = 1 << 19;
 // Largest supported expert count / top-k / shared experts.
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
@@ -52,6 +56,7 @@ struct Plan {
   int64_t pairs;     // T*k
   int64_t nblk;      // router blocks
   int rsplit;        // router workgroups per block (split K; 1 = one kernel)
+  int rwide;         // tokens per router workgroup of the wide split form (0: not used)
   int route_mode;    // kRouteSigmoid / kRouteRaw bits of the router options
   int cap;           // expert capacity in pairs (INT_MAX: no cut)
   int ffn_max;       // max(ffn, ffn_shared)

@@ -244,6 +244,78 @@ __global__ __launch_bounds__(64 * NW) void router_partial_kernel(
     dst[i] = lds[(i / ep) * ld + i % ep];
 }
 
+// Many tokens and a large router matrix: each workgroup of the one-kernel
+// router would stream the whole matrix for its 16 tokens (the DeepSeek-V3-
+// shaped router, 3.67 MB, 256 times over).  Here a workgroup takes 64 tokens
+// (four 16-token tiles, each weight fragment used for all four) over K part
+// blockIdx.x / ngroups of nsplit, and writes part[split][token][e] for the
+// finish kernel.  Wave w owns expert tiles w, w + 4, ... (NT of them); the K
+// loop issues U k-steps of loads per batch before their MFMAs.
+template <int NT>
+__global__ __launch_bounds__(256) void router_wide_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    int ngroups, int nsplit, float* __restrict__ part) {
+  constexpr int TT = 4, U = 4;
+  const int ep = ((E + 15) >> 4) * 16, etiles = ep >> 4;
+  // split fastest: with 8 (or 4) K parts, each XCD (workgroup i runs on XCD
+  // i % 8) reads one part of the router matrix, which stays in its L2
+  const int split = blockIdx.x % nsplit, grp = blockIdx.x / nsplit;
+  const int t0 = grp * (16 * TT);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint16_t* xp[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    int row = t0 + 16 * tt + (lane & 15);
+    row = row < T ? row : T - 1;
+    xp[tt] = x + (int64_t)row * d + (lane >> 4) * 8;
+  }
+  const uint16_t* wp[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    int e = (wave + 4 * i) * 16 + (lane & 15);
+    e = e < E ? e : E - 1;
+    wp[i] = wr + (int64_t)e * d + (lane >> 4) * 8;
+  }
+  f32x4 acc[TT][NT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[tt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = d >> 5;
+  const int c0 = split * nk / nsplit, c1 = (split + 1) * nk / nsplit;
+  for (int c = c0; c < c1; c += U) {
+    u32x4 a[U][TT], b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cu = min(c + u, c1 - 1);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) a[u][tt] = *(const u32x4*)(xp[tt] + cu * 32);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) b[u][i] = *(const u32x4*)(wp[i] + cu * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u >= c1) continue;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[tt][i] = mfma16(a[u][tt], b[u][i], acc[tt][i]);
+    }
+  }
+  // D[m = token][n = expert]: lane holds expert (lane & 15), tokens 4*(lane>>4)+r
+  float* dst = part + ((int64_t)split * ngroups * (16 * TT) + t0) * ep;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int tile = wave + 4 * i;
+    if (tile >= etiles) continue;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dst[(int64_t)(16 * tt + 4 * (lane >> 4) + r) * ep + tile * 16 + (lane & 15)] = acc[tt][i][r];
+  }
+}
+
 // Where the finish kernel runs the dispatch (null counts: it does not).
 struct FusedDispatch {
   int32_t *counts, *offsets, *sorted_token, *slot_row;
@@ -253,7 +325,8 @@ struct FusedDispatch {
 };
 
 // Adds the nsplit (<= kMaxRouterSplit) partial logits of a token block in
-// split order, then the same selection as the one-kernel router.  All
+// split order (partial q of token t at part[q * plane + t * ep + e]), then
+// the same selection as the one-kernel router.  All
 // partial loads of an element are issued before the first add, so the sum
 // costs one memory round trip.  With a single token block and fd.counts
 // set, the one workgroup then runs the whole dispatch (dispatch_body.h) on
@@ -263,14 +336,13 @@ struct FusedDispatch {
 // separate launch.)  kDispatchThreads threads; dynamic LDS: [16][ld] floats,
 // then sel[16*k].
 __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
-    const float* __restrict__ part, const float* __restrict__ bias, int mode, int T, int E, int k,
-    int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist, int32_t* blk_rank,
-    FusedDispatch fd) {
+    const float* __restrict__ part, int64_t plane, const float* __restrict__ bias, int mode, int T,
+    int E, int k, int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist,
+    int32_t* blk_rank, FusedDispatch fd) {
   extern __shared__ float lds[];
   const int ep = ((E + 15) >> 4) * 16, ld = ep + 4;
   int32_t* sel = (int32_t*)(lds + kRouterTokens * ld);
   const int t0 = blockIdx.x * kRouterTokens;
-  const int64_t plane = (int64_t)nblk * kRouterTokens * ep;
   const float* src = part + (int64_t)t0 * ep;
   for (int i = threadIdx.x; i < kRouterTokens * ep; i += blockDim.x) {
     float v[kMaxRouterSplit];
@@ -361,6 +433,31 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
   const size_t lds = (size_t)KS * kRouterTokens * ld * 4 + sel_bytes;
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)w_router;
+  const int64_t ep = etiles * 16;
+  if (P.rwide) {
+    const int ngroups = (int)((D.T + P.rwide - 1) / P.rwide);
+    const dim3 pgrid((unsigned)(ngroups * P.rsplit));
+    auto partial = [&](auto kern) {
+      hipLaunchKernelGGL(kern, pgrid, dim3(256), 0, s, xb, wb, (int)D.T, D.d, D.E, ngroups,
+                         P.rsplit, part);
+    };
+    const int ntw = (etiles + 3) / 4;
+    if (ntw <= 1)
+      partial(router_wide_partial_kernel<1>);
+    else if (ntw <= 2)
+      partial(router_wide_partial_kernel<2>);
+    else if (ntw <= 4)
+      partial(router_wide_partial_kernel<4>);
+    else
+      partial(router_wide_partial_kernel<8>);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
+                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
+                       (int64_t)ngroups * P.rwide * ep, bias, P.route_mode, (int)D.T, D.E, D.k,
+                       (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, FusedDispatch{});
+    return hipGetLastError();
+  }
   if (P.rsplit > 1) {
     FusedDispatch fd{};
     if (dout && P.nblk == 1) {
@@ -384,8 +481,9 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
-                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part, bias, P.route_mode,
-                       (int)D.T, D.E, D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
+                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
+                       (int64_t)P.nblk * kRouterTokens * ep, bias, P.route_mode, (int)D.T, D.E,
+                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
     return hipGetLastError();
   }
   auto args = [&](auto kern) {

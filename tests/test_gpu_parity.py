@@ -46,6 +46,9 @@ SMALL = {c.name: c for c in [
            bias="normal", bias_var=0.5),
     # several token blocks with the router K split over workgroups, two shared experts
     custom("split_router", 115, T=100, d=512, E=16, k=2, ffn=64, n_shared=2, ffn_shared=64),
+    # many tokens and a large router matrix (E * d >= 2^19): the wide router
+    # (64-token workgroups over K parts); T not a multiple of 64
+    custom("wide_router", 116, T=300, d=4096, E=128, k=4, ffn=64, bias="normal", bias_var=0.5),
     NAMED["tiny_f32"],
 ]}
 
@@ -117,23 +120,38 @@ def test_steps_small(name):
     assert np.array_equal(stok.cpu().numpy(), exp_stok)
     assert np.array_equal(slot.cpu().numpy().ravel(), exp_slot)
 
-    # experts on the oracle's grouping
+    # experts on the oracle's grouping.  For bf16 layers the kernels round h
+    # to bf16 (half an ulp: 2^-9 relative) before the down GEMM, so each
+    # expert output may differ from the fp64 value by up to
+    # 2^-9 * sum_j |h_j| |W_down[:, j]|; the check allows twice that (fp32
+    # accumulation adds far less) on every element.  (The layer output y,
+    # checked above and below, keeps the rms bar.)
     X = oracle.widen(c.x, cfg.dtype)
+    exp_out = bound = None
     for path in paths(cfg):
         out = moe.moe_experts(x, W, k, torch.from_numpy(exp_offs).cuda(),
                               torch.from_numpy(exp_stok).cuda(), path=path)
         torch.cuda.synchronize()
         out = out.cpu().numpy()
-        exp_out = np.empty_like(out, dtype=np.float64)
-        for g in range(E + cfg.n_shared):
-            r0, r1 = exp_offs[g], exp_offs[g + 1]
-            if r1 == r0:
-                continue
-            ws = c.expert(g) if g < E else c.shared(g - E)
-            exp_out[r0:r1] = oracle.swiglu_expert(X[exp_stok[r0:r1]],
-                                                  *(oracle.widen(a, cfg.dtype) for a in ws))
+        if exp_out is None:
+            exp_out = np.zeros_like(out, dtype=np.float64)
+            bound = np.zeros_like(exp_out)
+            for g in range(E + cfg.n_shared):
+                r0, r1 = exp_offs[g], exp_offs[g + 1]
+                if r1 == r0:
+                    continue
+                wu, wg, wd = (oracle.widen(a, cfg.dtype)
+                              for a in (c.expert(g) if g < E else c.shared(g - E)))
+                Xg = X[exp_stok[r0:r1]]
+                exp_out[r0:r1] = oracle.swiglu_expert(Xg, wu, wg, wd)
+                H = oracle.silu(Xg @ wg.T) * (Xg @ wu.T)
+                bound[r0:r1] = 2.0 ** -8 * (np.abs(H) @ np.abs(wd).T)
         err = rel_err(out, exp_out)
-        assert err <= TOL[cfg.dtype], (path, err)
+        if cfg.dtype == "bf16":
+            excess = np.abs(out.astype(np.float64) - exp_out) - bound
+            assert excess.max() <= 1e-6 * np.sqrt(np.mean(exp_out ** 2)), (path, excess.max())
+        else:
+            assert err <= TOL[cfg.dtype], (path, err)
 
     # combine on the oracle's expert outputs and weights
     out_ref = torch.from_numpy(exp_out.astype(np.float32)).cuda()

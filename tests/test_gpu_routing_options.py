@@ -55,6 +55,9 @@ CASES = {
     "f32_sigmoid_capacity": (custom("f32_sigmoid_capacity", 139, T=70, d=64, E=6, k=2, ffn=36,
                                     dtype="f32", bias="normal", bias_var=0.05),
                              Options(scoring="sigmoid", renormalize=False, capacity_factor=0.8)),
+    # the wide router form with sigmoid scores and raw weights
+    "sigmoid_wide": (custom("sigmoid_wide", 141, T=260, d=4096, E=128, k=4, ffn=64,
+                            bias="normal", bias_var=0.02), SIG_RAW),
     # long K: the down GEMM splits K; dropped pairs skip their partial rows too
     "capacity_ksplit": (custom("capacity_ksplit", 140, T=200, d=128, E=3, k=2, ffn=8192,
                                bias="normal", bias_var=1.0), Options(capacity_factor=0.9)),
