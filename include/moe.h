@@ -170,6 +170,8 @@ int64_t moe_grouped_rows(const moe_desc* desc);
  *   expert_counts [E] int32       optional output: (token, slot) pairs routed to
  *                                 each expert (before any capacity cut)
  *   workspace    >= moe_workspace_size(desc) bytes, 256-byte aligned
+ * x, w_router and the expert weight arrays are 16-byte aligned (the kernels
+ * read them in 16-byte chunks; MOE_ERR_INVALID_ARG otherwise).
  * A layer with MXFP4 experts needs moe_forward_mx (MOE_ERR_INVALID_ARG here).
  */
 int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
@@ -194,8 +196,8 @@ typedef struct moe_mx_scales {
 /*
  * moe_forward for a layer with expert_format MOE_EXPERTS_MXFP4: w_up, w_gate
  * [E,ffn,d/2], w_down [E,d,ffn/2] (and the shared counterparts) hold the
- * packed E2M1 codes, `scales` their E8M0 scales.  Every other argument is as
- * for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
+ * packed E2M1 codes, `scales` their E8M0 scales (16-byte aligned like the
+ * codes).  Every other argument is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
  * moe_forward_timed.  Scale bytes 0 (2^-127) and 255 (NaN) follow the format
  * but results that leave bfloat16's normal range are not defined.
  */
@@ -227,6 +229,7 @@ int moe_forward_timed(const moe_desc* desc, const void* x, const void* w_router,
  * Logits are accumulated in float32; selection compares float32 keys (the
  * logits, or sigmoid scores plus bias), ties to the lower index.
  *   topk_idx [T,k] int32 (required), topk_w [T,k] float32 (required).
+ * x and w_router are 16-byte aligned (MOE_ERR_INVALID_ARG otherwise).
  */
 int moe_route(const moe_desc* desc, const void* x, const void* w_router,
               const float* router_bias, int32_t* topk_idx, float* topk_w,
@@ -257,7 +260,8 @@ int moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* expert_
  * down).  For grouped row r of group g with token t = sorted_token[r]:
  *   expert_out[r,:] = FFN_g(x[t,:])       float32 [T*(k+n_shared), d]
  * group_offsets / sorted_token as produced by moe_dispatch.  Dense expert
- * weights only (MOE_ERR_INVALID_ARG for MXFP4).
+ * weights only (MOE_ERR_INVALID_ARG for MXFP4).  x and the weight arrays are
+ * 16-byte aligned (MOE_ERR_INVALID_ARG otherwise).
  */
 int moe_experts(const moe_desc* desc, const void* x, const void* w_up, const void* w_gate,
                 const void* w_down, const void* ws_up, const void* ws_gate,

@@ -2,6 +2,8 @@
 // checks, workspace carving and the launch sequence on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "kernels.h"
 #include "plan.h"
 
@@ -39,6 +41,13 @@ bool shared_ok(const moe_desc* d, const void* a, const void* b, const void* c) {
   return d->n_shared == 0 || (a && b && c);
 }
 
+// Token, weight and scale arrays are read in 16-byte chunks.
+bool a16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 15) return false;
+  return true;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -63,6 +72,9 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
   if (!x || !w_router || !w_up || !w_gate || !w_down || !y) return MOE_ERR_INVALID_ARG;
   if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
   if (mx && (!mx->up || !mx->gate || !mx->down || !shared_ok(d, mx->s_up, mx->s_gate, mx->s_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (!a16({x, w_router, w_up, w_gate, w_down, ws_up, ws_gate, ws_down}) ||
+      (mx && !a16({mx->up, mx->gate, mx->down, mx->s_up, mx->s_gate, mx->s_down})))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) -> hipError_t {
@@ -157,6 +169,7 @@ int moe_route(const moe_desc* d, const void* x, const void* w_router, const floa
   int st = prepare(d, workspace, workspace_bytes, &P, &empty);
   if (st != MOE_OK || empty) return st;
   if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!a16({x, w_router})) return MOE_ERR_INVALID_ARG;
   Ws W{(char*)workspace};
   MOE_TRY(launch_router(P, x, w_router, router_bias, topk_idx, topk_w,
                         W.at<int32_t>(P.o_blk_hist), W.at<int32_t>(P.o_blk_rank),
@@ -196,6 +209,7 @@ int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* 
   if (!x || !w_up || !w_gate || !w_down || !group_offsets || !sorted_token || !expert_out)
     return MOE_ERR_INVALID_ARG;
   if (!shared_ok(d, ws_up, ws_gate, ws_down)) return MOE_ERR_INVALID_ARG;
+  if (!a16({x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down})) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   Ws W{(char*)workspace};
   Tile* tu = W.at<Tile>(P.o_tiles_up);

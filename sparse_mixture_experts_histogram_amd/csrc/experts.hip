@@ -743,6 +743,208 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
   }
 }
 
+// MXFP4 weights through LDS, for batches with about one (token, expert) pair
+// per expert and more: a tile is 16 rows x 16 NW features, one wave per 16
+// features over the whole of K, so the token slab in LDS is shared by NW
+// waves (the direct-load kernel above re-reads it per wave).  K streams in
+// stages of 256 (eight 32-k blocks) through a 3-stage ring of LDS copies: a
+// stage holds the 16 x 256 token slab (8 KB, every wave copies 8 KB / NW
+// of it) and, per wave and weight matrix, 16 feature rows x 128 code bytes
+// (a copy instruction moves 128 contiguous bytes of 8 rows).  The tile's
+// E8M0 scales (16 NW rows x K/32 bytes, one contiguous block in HBM) are
+// copied to LDS once, before the ring starts, so no load into registers
+// sits between the copies in flight (the compiler would then wait for all
+// of them).  Lane (r, g) feeds k 32 j + 8 g + (0..7) of block j: codes dword
+// g of feature row r's block j, widened with the row's block scale, and
+// token row r.  16-byte chunks sit XOR-swizzled in LDS (codes: chunk c of
+// row r at c ^ (r / 2) % 8; tokens: chunk c at c ^ r % 16) so fragment
+// reads spread over the banks.  Blocks past K copy a clamped chunk and
+// their codes are zeroed; waves past N (a partial tile) re-read the last
+// row and store nothing.  Needs K a multiple of 64 and at most kMxLdsMaxK.
+template <bool UPGATE, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
+  constexpr int NS = UPGATE ? 2 : 1;
+  constexpr int XS = 16 * 256;               // token stage, bf16 elements (8 KB)
+  constexpr int XI = 8 / NW;                 // token copies per wave and stage
+  constexpr int CS = NW * NS * 2048;         // code stage, bytes (2 KB per wave and matrix)
+  constexpr int SCS = 16 * NW * (kMxLdsMaxK / 32);  // scales of one matrix, bytes
+  constexpr int NLD = XI + 2 * NS;           // copies per wave and stage
+  static_assert(NW == 4 || NW == 8, "the token slab splits into 1 KB copies per wave");
+  const int L = tile_of_block(a.tiles);
+  if (L < 0) return;
+  const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
+  Tile tl = uniform_tile(a.tiles[1 + L % mtot]);
+  tl.n0 = (L / mtot) * (16 * NW);
+  const bool sh = tl.g >= a.E;
+  const int N = sh ? a.N_s : a.N_r;
+  const int K = sh ? a.K_s : a.K_r;
+  if (tl.n0 >= N) return;
+  const int ge = sh ? tl.g - a.E : tl.g;
+  const int nb = K >> 5;                 // 32-k blocks
+  const int nst = (nb + 7) >> 3;         // 256-k stages
+  const int64_t cstride = (int64_t)N * (K / 2), sstride = (int64_t)N * nb;
+  // one named array per stage, so the compiler tells reads of one stage
+  // from copies still landing in another
+  __shared__ __attribute__((aligned(1024))) uint16_t lx0[XS], lx1[XS], lx2[XS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lc0[CS], lc1[CS], lc2[CS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lsc[NS * SCS];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // token copy: instruction i of wave w fills 1 KB block b = w + NW i, rows
+  // 2 b + l / 32; lane l takes LDS slot l % 32 of its row, global chunk
+  // slot ^ row % 16
+  const uint16_t* xsrc[XI];
+  int xchunk[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int xr = 2 * (wave + NW * i) + (lane >> 5);
+    int xrow = tl.m0 + xr;
+    xrow = xrow < tl.m_end ? xrow : tl.m_end - 1;
+    const int64_t xtok = a.sorted ? (int64_t)a.sorted[xrow] : (int64_t)xrow;
+    xsrc[i] = a.tok + xtok * a.ldt;
+    xchunk[i] = (lane & 31) ^ (xr & 15);
+  }
+  // code copy: instruction i of a matrix holds feature rows 16 w + 8 i + l / 8;
+  // lane l takes slot l % 8, global chunk (32-k block of the stage) slot ^ (row / 2) % 8
+  const uint8_t* csrc[NS][2];
+  int cchunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cr = 8 * i + (lane >> 3);
+    cchunk[i] = (lane & 7) ^ ((cr >> 1) & 7);
+    int64_t cn = tl.n0 + 16 * wave + cr;
+    cn = cn < N ? cn : N - 1;
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      csrc[q][i] = (const uint8_t*)(q == 0 ? (sh ? a.s0 : a.w0) : (sh ? a.s1 : a.w1)) +
+                   ge * cstride + cn * (K / 2);
+  }
+  // the row lookups above have landed before any copy is issued (a load
+  // into registers behind copies in flight would wait for all of them)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_sched_barrier(0);
+  // scales: the tile's rows x nb bytes of each matrix, 1 KB per copy
+  // instruction, instruction i by wave i % NW (chunks past the end clamped)
+  {
+    const int rows = min(16 * NW, N - tl.n0);  // a multiple of 64, as N is
+    const int nch = rows * nb / 16, ni = (nch + 63) >> 6;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const uint8_t* src =
+          (q == 0 ? (sh ? a.ss0 : a.sw0) : (sh ? a.ss1 : a.sw1)) + ge * sstride + (int64_t)tl.n0 * nb;
+      for (int i = wave; i < ni; i += NW) {
+        int c = 64 * i + lane;
+        c = c < nch ? c : nch - 1;
+        __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c),
+                                         LDS_PTR(lsc + q * SCS + i * 1024), 16, 0, 0);
+      }
+    }
+  }
+  // all copies of stage st (clamped past the end: a re-fetch into a dead stage)
+  auto issue = [&](int st, uint16_t* lx, uint8_t* lc) {
+    st = st < nst ? st : nst - 1;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      int c = 32 * st + xchunk[i];           // 8-k chunk along the token row
+      c = c < (K >> 3) ? c : (K >> 3) - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + c * 8),
+                                       LDS_PTR(lx + (wave + NW * i) * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int b = 8 * st + cchunk[i];          // 32-k block = 16-byte code chunk
+        b = b < nb ? b : nb - 1;
+        __builtin_amdgcn_global_load_lds((const void*)(csrc[q][i] + b * 16),
+                                         LDS_PTR(lc + (wave * NS + q) * 2048 + i * 1024), 16,
+                                         0, kWeightPolicy);
+      }
+  };
+  f32x4 acc[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r = lane & 15, g = lane >> 4;
+  const int srow = (16 * wave + r) * nb;     // this lane's scale row in LDS
+  auto compute = [&](int st, const uint16_t* xs, const uint8_t* lc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool live = 8 * st + j < nb;
+      const int xoff = r * 256 + (((4 * j + g) ^ r) << 3);
+      const u32x4 fx = *(const u32x4*)(xs + xoff);
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int coff = (wave * NS + q) * 2048 + r * 128 + ((j ^ ((r >> 1) & 7)) << 4) + 4 * g;
+        uint32_t w = *(const uint32_t*)(lc + coff);
+        const int bj = min(8 * st + j, nb - 1);
+        const uint32_t byte = lsc[q * SCS + srow + bj];
+        asm volatile("" ::: "memory");  // keep reads of different arrays apart (a
+                                        // merged read carries no alias information)
+        w = live ? w : 0u;
+        const float scale =
+            __uint_as_float(byte == 0 ? 0x00400000u : byte == 255 ? 0x7FC00000u : byte << 23);
+        u32x4 fa;
+        fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        fa[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        fa[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        fa[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+        acc[q] = mfma16(fa, fx, acc[q]);
+      }
+    }
+  };
+  // this wave's copies of the stage to read (and every older copy, the
+  // scales included) have landed, then all waves'; a plain barrier (a
+  // fenced one would wait for every copy in flight)
+  auto wait_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue(0, lx0, lc0);
+  issue(1, lx1, lc1);
+  int st = 0;
+  for (; st + 3 <= nst; st += 3) {
+    wait_stage();
+    issue(st + 2, lx2, lc2);
+    compute(st, lx0, lc0);
+    wait_stage();
+    issue(st + 3, lx0, lc0);
+    compute(st + 1, lx1, lc1);
+    wait_stage();
+    issue(st + 4, lx1, lc1);
+    compute(st + 2, lx2, lc2);
+  }
+  if (st < nst) {
+    wait_stage();
+    issue(st + 2, lx2, lc2);
+    compute(st, lx0, lc0);
+    if (st + 1 < nst) {
+      wait_stage();
+      compute(st + 1, lx1, lc1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
+  // D[n = feature][m = row]: lane holds row (lane & 15), features 4*(lane>>4)+0..3
+  const int nn = tl.n0 + 16 * wave + 4 * (lane >> 4);
+  const int orow = tl.m0 + (lane & 15);
+  if (orow >= tl.m_end || nn >= N) return;
+  if (UPGATE) {
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(silu_mul(acc[1][0], acc[0][0])) |
+           ((uint32_t)f32_to_bf16(silu_mul(acc[1][1], acc[0][1])) << 16);
+    pk.y = (uint32_t)f32_to_bf16(silu_mul(acc[1][2], acc[0][2])) |
+           ((uint32_t)f32_to_bf16(silu_mul(acc[1][3], acc[0][3])) << 16);
+    *(uint2*)((uint16_t*)a.out + (int64_t)orow * a.ldo + nn) = pk;
+  } else {
+    *(float4*)((float*)a.out + (int64_t)orow * a.ldo + nn) =
+        make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  }
+}
+
+
 // ---------------------------------------------------------------- float32
 // Plain VALU tiles (32 rows x 32 features, K slabs of 16, the last one
 // zero-padded) in float32.
@@ -871,7 +1073,10 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, block, 0, s, u);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP4)
+  if (P.kind == KIND_MXFP4 && P.up.bn == 16 * kMxUpWaves)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMxUpWaves>), grid, dim3(64 * kMxUpWaves), 0, s,
+                       up_args(P, x));
+  else if (P.kind == KIND_MXFP4)
     hipLaunchKernelGGL(gemm_mx_stream_kernel<true>, grid, block, 0, s, up_args(P, x));
   else if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
@@ -894,7 +1099,10 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, block, 0, s, dn);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP4)
+  if (P.kind == KIND_MXFP4 && P.down.bn == 16 * kMxDownWaves)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMxDownWaves>), grid, dim3(64 * kMxDownWaves), 0,
+                       s, down_args(P, x));
+  else if (P.kind == KIND_MXFP4)
     hipLaunchKernelGGL(gemm_mx_stream_kernel<false>, grid, block, 0, s, down_args(P, x));
   else if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));

@@ -14,19 +14,31 @@ namespace moe {
 static int prefill_rows(const moe_desc* d) {
   return d->T * d->k >= 384LL * d->E ? 256 : 128;
 }
-// The streaming kernels use 16-row tiles of 16 (bf16) or 32 (MXFP4) columns.
+// The streaming kernels use 16-row tiles of 16 (bf16) or 32 (MXFP4) columns;
+// MXFP4 layers with at least one (token, expert) pair per expert and a
+// reduction of at most kMxLdsMaxK use the LDS-staged kernel's wider tiles
+// (measured on the gpt-oss-shaped layer: faster from 32 tokens on, slower
+// at 1).
 static bool streaming(int kind) { return kind == KIND_BF16_DECODE || kind == KIND_MXFP4; }
+static bool mx_lds(const moe_desc* d, int K) {
+  return (int64_t)d->T * d->k >= d->E && K <= kMxLdsMaxK;
+}
+static int down_k(const moe_desc* d) {
+  return d->n_shared && d->ffn_shared > d->ffn ? d->ffn_shared : d->ffn;
+}
 int up_row_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? prefill_rows(d) : streaming(kind) ? 16 : 32;
 }
 int up_col_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? 128 : kind == KIND_MXFP4 ? 32 : streaming(kind) ? 16 : 32;
+  if (kind == KIND_MXFP4) return mx_lds(d, d->d) ? 16 * kMxUpWaves : 32;
+  return kind == KIND_BF16_PREFILL ? 128 : streaming(kind) ? 16 : 32;
 }
 int down_row_tile(int kind, const moe_desc* d) {
   return kind == KIND_BF16_PREFILL ? prefill_rows(d) : streaming(kind) ? 16 : 32;
 }
 int down_col_tile(int kind, const moe_desc* d) {
-  return kind == KIND_BF16_PREFILL ? 256 : kind == KIND_MXFP4 ? 32 : streaming(kind) ? 16 : 32;
+  if (kind == KIND_MXFP4) return mx_lds(d, down_k(d)) ? 16 * kMxDownWaves : 32;
+  return kind == KIND_BF16_PREFILL ? 256 : streaming(kind) ? 16 : 32;
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

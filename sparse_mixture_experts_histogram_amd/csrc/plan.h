@@ -26,6 +26,11 @@ constexpr int kMaxShared = 8;
 constexpr int kRowSlack = 256;
 // Router option bits: sigmoid scores with a selection-only bias; raw weights.
 constexpr int kRouteSigmoid = 1, kRouteRaw = 2;
+// MXFP4 experts: the LDS-staged kernel takes reductions up to this long, in
+// tiles of 16 x 16 W features (W waves: kMxUpWaves for up/gate,
+// kMxDownWaves for down); the direct-load kernel takes 16 x 32 tiles.
+constexpr int kMxLdsMaxK = 3072;
+constexpr int kMxUpWaves = 8, kMxDownWaves = 4;
 
 // One GEMM tile: rows [m0, m_end) of group g, output columns [n0, n0 + BN).
 // Entry 0 of a schedule is a header: {entries, row tiles, column tiles, 0}.

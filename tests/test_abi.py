@@ -110,6 +110,16 @@ def test_entry_points_reject_before_launch():
     misaligned = ctypes.c_void_p((1 << 20) + 16)
     assert L.moe_route(ctypes.byref(d), None, None, None, None, None, misaligned, n.value,
                        None) == WORKSPACE
+    # token / weight arrays must be 16-byte aligned (fake pointers, never dereferenced)
+    a = [ctypes.c_void_p((2 << 20) + 4096 * i) for i in range(6)]
+    odd = ctypes.c_void_p((3 << 20) + 8)
+    args = [a[0], a[1], None, a[2], a[3], a[4], None, None, None, a[5], None, None, None]
+    for i in (0, 1, 3, 4, 5):
+        bent = list(args)
+        bent[i] = odd
+        assert L.moe_forward(ctypes.byref(d), *bent, fake, n.value, None) == INVALID, i
+    assert L.moe_route(ctypes.byref(d), odd, a[1], None, a[2], a[3], fake, n.value,
+                       None) == INVALID
     bad = desc(k=0)
     assert L.moe_combine(ctypes.byref(bad), None, None, None, None, None, None) == INVALID
     assert L.moe_status_str(-3).startswith(b"MOE_ERR_WORKSPACE")

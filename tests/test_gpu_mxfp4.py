@@ -21,14 +21,24 @@ from moe_inputs import NAMED, generate, tables
 
 pytestmark = pytest.mark.gpu
 
+# Two kernels run MXFP4 experts: the direct-load one (fewer (token, expert)
+# pairs than experts, or K above 3072) and the LDS-staged one (16 x 128 up/gate
+# tiles, 16 x 64 down tiles, K in stages of 256 through a 3-slot ring).
+# mx_one_token and the gpt-oss T=1 and T=8 layers take the first;
+# mx_long_k takes it for up/gate only; the rest take the second: mx_ragged
+# and mx_shared with partial 128-feature tiles, mx_stages with 5 and 4
+# stages (the ring's two tail forms), mx_k2880 with a last stage of 2 blocks.
+# In the direct-load kernel K = 2880 (45 units of 64) splits over four waves
+# in ranges that are not multiples of its load batch.
 SMALL = {c.name: c for c in [
     custom("mx_ragged", 150, T=150, d=256, E=8, k=2, ffn=192),
     custom("mx_shared", 151, T=70, d=128, E=16, k=4, ffn=64, n_shared=1, ffn_shared=128,
            bias="normal", bias_var=0.5),
     custom("mx_one_token", 152, T=1, d=192, E=8, k=2, ffn=128),
     custom("mx_k_equals_e", 153, T=33, d=64, E=4, k=4, ffn=64),
-    # K of 45 64-wide units: the four waves' ranges are not multiples of the load batch
     custom("mx_k2880", 154, T=40, d=2880, E=4, k=2, ffn=2880),
+    custom("mx_stages", 155, T=64, d=1280, E=8, k=2, ffn=1024),
+    custom("mx_long_k", 156, T=24, d=4096, E=4, k=2, ffn=128),
 ]}
 
 
@@ -103,10 +113,12 @@ def test_mxfp4_rejects_dense_entry_points():
                             None, None, None, None, 0, None, None) == -1
 
 
-@pytest.mark.parametrize("T", [1, 8, 128])
+@pytest.mark.parametrize("T", [1, 8, 32, 128])
 def test_mxfp4_gpt_oss_full_size(T):
     """The gpt-oss-shaped layer (d=2880, 128 experts, top-4) with MXFP4
-    experts at decode batch sizes: routing on every token, y on samples."""
+    experts at decode batch sizes: routing on every token, y on samples
+    (T = 32 is the first batch with as many pairs as experts, where the
+    LDS-staged kernel takes over)."""
     cfg = NAMED["gpt_oss"]
     li = tables.layer_inputs(cfg, T)
     c = MxCase(cfg, T, x=li.x)
