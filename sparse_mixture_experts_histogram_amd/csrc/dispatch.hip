@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
 __global__ __launch_bounds__(kDispatchThreads) void tiles_kernel(const int32_t* __restrict__ offsets,
                                                                  int G, Tile* tiles_up, TileCfg cu,
                                                                  Tile* tiles_down, TileCfg cd) {
-  __shared__ int scan_buf[2 * kDispatchThreads];
+  __shared__ int scan_buf[kDispatchThreads / 64];
   __shared__ int goff[kMaxGroups + 1];
   __shared__ int gsize[kMaxGroups];
   __shared__ int mb_up[kMaxGroups + 1];

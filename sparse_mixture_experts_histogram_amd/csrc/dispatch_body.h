@@ -39,25 +39,32 @@ struct TileCfg {
   int bm, bn, n_tiles, row_list, n_fastest;
 };
 
-// Inclusive scan of v over the block (kDispatchThreads entries, one per
-// thread); returns the exclusive prefix.  buf has 2*kDispatchThreads ints.
-__device__ inline int block_excl_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  int* a = buf;
-  int* b = buf + kDispatchThreads;
-  a[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kDispatchThreads; off <<= 1) {
-    b[tid] = a[tid] + (tid >= off ? a[tid - off] : 0);
-    __syncthreads();
-    int* t = a;
-    a = b;
-    b = t;
+// Exclusive scan of v over the block (kDispatchThreads entries, one per
+// thread, in thread order); *total receives the sum.  A shuffle scan inside
+// each wave, then every thread adds the totals of the waves before it: two
+// barriers instead of one per doubling step.  buf holds at least
+// kDispatchThreads / 64 ints.
+__device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
+  constexpr int NWV = kDispatchThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int incl = a[tid];
-  *total = a[kDispatchThreads - 1];
+  if (lane == 63) buf[wave] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const int t = buf[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  *total = all;
+  __syncthreads();  // buf is free again
+  return before + x - v;
 }
 
 // Tile schedule of one grouped GEMM.  Group g has mt_g = ceil(size_g / bm)
@@ -66,7 +73,7 @@ __device__ inline int block_excl_scan(int v, int* buf, int* total) {
 // (row tile fastest), so the workgroups that run together on one XCD share
 // both the weight tiles and the token tiles through that XCD's L2.
 // tiles[0] = {entry count, row tiles, column tiles, 0}.
-__device__ inline void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
+__device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
                             TileCfg c, Tile* tiles) {
   const int total = mtot * c.n_tiles;
   if (threadIdx.x == 0) tiles[0] = Tile{total, mtot, c.n_tiles, 0};
@@ -101,15 +108,15 @@ __device__ inline void build_tiles(const int* goff, const int* gsize, const int*
 }
 
 // The whole dispatch, run by one workgroup of kDispatchThreads threads.
-// (No __restrict__: in the router's fused form the same workgroup has just
-// written idx, blk_hist and blk_rank through other pointers.)
-__device__ inline void dispatch_body(
+// (No __restrict__: in the router's fused form idx, blk_hist and blk_rank
+// are LDS arrays the same workgroup has just written.)
+__device__ __forceinline__ void dispatch_body(
     const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
     int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
     int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
     TileCfg cd) {
   __shared__ int part[kDispatchThreads];
-  __shared__ int scan_buf[2 * kDispatchThreads];
+  __shared__ int scan_buf[kDispatchThreads / 64];
   __shared__ int goff[kMaxGroups + 1];
   __shared__ int gsize[kMaxGroups];
   __shared__ int mb_up[kMaxGroups + 1];
@@ -117,17 +124,22 @@ __device__ inline void dispatch_body(
   const int tid = threadIdx.x;
   const int G = E + n_sh;
 
-  // 1. column scans of the block histogram
+  // 1. column scans of the block histogram: expert e's column is split into
+  // S segments of about kBatch blocks (at most kDispatchThreads / Ep), one
+  // thread each; a thread per expert then walks the S segment sums in order.
+  // (S is not simply kDispatchThreads / Ep: with few blocks that serial walk
+  // over mostly empty segments was most of the dispatch time.)
+  constexpr int kBatch = 16;
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
-  const int S = kDispatchThreads / Ep;
+  const int S = min(kDispatchThreads / Ep, max(1, (nblk + kBatch - 1) / kBatch));
   const int e = tid % Ep, seg = tid / Ep;
-  const int b0 = (int)((int64_t)seg * nblk / S), b1 = (int)((int64_t)(seg + 1) * nblk / S);
+  const int b0 = seg < S ? (int)((int64_t)seg * nblk / S) : 0;
+  const int b1 = seg < S ? (int)((int64_t)(seg + 1) * nblk / S) : 0;
   // (Loads go in batches of kBatch independent loads: a thread walks up to
   // nblk / S blocks, and one memory round trip per block was most of the
   // dispatch time for many blocks and experts.)
-  constexpr int kBatch = 16;
-  if (e < E) {
+  if (e < E && seg < S) {
     int s = 0;
     for (int b = b0; b < b1; b += kBatch) {
       int v[kBatch];
@@ -150,7 +162,7 @@ __device__ inline void dispatch_body(
     counts[tid] = run;
   }
   __syncthreads();
-  if (e < E) {
+  if (e < E && seg < S) {
     int run = part[seg * Ep + e];
     for (int b = b0; b < b1; b += kBatch) {
       int v[kBatch];

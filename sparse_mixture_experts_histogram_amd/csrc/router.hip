@@ -34,24 +34,39 @@ namespace moe {
 
 // Histogram of one block's pairs and each pair's rank among earlier pairs of
 // the same expert (sel holds the block's n_pairs expert ids in pair order).
-__device__ void block_hist_rank(const int32_t* sel, int n_pairs, int E, int32_t* hist_out,
+// The pairs are compared in batches of 16 independent LDS reads (a loop of
+// one dependent read per pair was most of the router's tail time).
+__device__ __forceinline__ void block_hist_rank(const int32_t* sel, int n_pairs, int E, int32_t* hist_out,
                                 int32_t* rank_out) {
+  constexpr int B = 16;
   for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
     const int e = sel[p];
     int r = 0;
-    for (int q = 0; q < p; ++q) r += (sel[q] == e);
+    for (int q0 = 0; q0 < p; q0 += B) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = q0 + i < p ? sel[q0 + i] : -1;
+#pragma unroll
+      for (int i = 0; i < B; ++i) r += (v[i] == e);
+    }
     rank_out[p] = r;
   }
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int c = 0;
-    for (int q = 0; q < n_pairs; ++q) c += (sel[q] == e);
+    for (int q0 = 0; q0 < n_pairs; q0 += B) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = q0 + i < n_pairs ? sel[q0 + i] : -1;
+#pragma unroll
+      for (int i = 0; i < B; ++i) c += (v[i] == e);
+    }
     hist_out[e] = c;
   }
 }
 
 // Top-k of the tokens of one block from LDS logits lg[tl*ld + e].
 template <int EPL>
-__device__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int mode,
+__device__ __forceinline__ void topk_block(const float* lg, int ld, const float* __restrict__ bias, int mode,
                            int t0, int T, int E, int k, int32_t* __restrict__ idx_out,
                            float* __restrict__ w_out, int32_t* sel) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -116,28 +131,38 @@ __device__ void topk_block(const float* lg, int ld, const float* __restrict__ bi
   }
 }
 
+// Top-k, then this block's histogram and ranks into hist_out[E] and
+// rank_out[pairs of the block] (global memory, or LDS in the fused dispatch).
 template <int EPL>
-__device__ void router_tail(float* lg, int ld, int32_t* sel, const float* bias, int mode, int t0,
+__device__ __forceinline__ void router_tail(float* lg, int ld, int32_t* sel, const float* bias, int mode, int t0,
                             int T, int E, int k, int32_t* idx_out, float* w_out,
-                            int32_t* blk_hist, int32_t* blk_rank) {
+                            int32_t* hist_out, int32_t* rank_out) {
   topk_block<EPL>(lg, ld, bias, mode, t0, T, E, k, idx_out, w_out, sel);
   __syncthreads();
   const int nt = min(kRouterTokens, T - t0);
-  block_hist_rank(sel, nt * k, E, blk_hist + (int64_t)blockIdx.x * E,
-                  blk_rank + (int64_t)t0 * k);
+  block_hist_rank(sel, nt * k, E, hist_out, rank_out);
 }
 
-__device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const float* bias, int mode,
+__device__ __forceinline__ void router_tail_to(float* lg, int ld, int32_t* sel, const float* bias, int mode,
+                               int t0, int T, int E, int k, int32_t* idx_out, float* w_out,
+                               int32_t* hist_out, int32_t* rank_out) {
+  if (E <= 64)
+    router_tail<1>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, hist_out, rank_out);
+  else if (E <= 128)
+    router_tail<2>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, hist_out, rank_out);
+  else if (E <= 256)
+    router_tail<4>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, hist_out, rank_out);
+  else
+    router_tail<8>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, hist_out, rank_out);
+}
+
+// The usual tail: the block's histogram and ranks go to global memory for
+// the dispatch kernel.
+__device__ __forceinline__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const float* bias, int mode,
                                      int t0, int T, int E, int k, int32_t* idx_out, float* w_out,
                                      int32_t* blk_hist, int32_t* blk_rank) {
-  if (E <= 64)
-    router_tail<1>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
-  else if (E <= 128)
-    router_tail<2>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
-  else if (E <= 256)
-    router_tail<4>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
-  else
-    router_tail<8>(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist, blk_rank);
+  router_tail_to(lg, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out,
+                 blk_hist + (int64_t)blockIdx.x * E, blk_rank + (int64_t)t0 * k);
 }
 
 // Logits of the kRouterTokens tokens from t0 over k-steps [kb0, kb1) (32 k
@@ -145,7 +170,7 @@ __device__ void router_tail_dispatch(float* lg, int ld, int32_t* sel, const floa
 // tiles [KS][16][ld]).  NW waves: wave w sums K part w % KS of the expert
 // tiles w / KS + i NW / KS; the KS partial tiles are then added in order.
 template <int NT, int NW>
-__device__ void block_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+__device__ __forceinline__ void block_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                              int T, int d, int E, int KS, int t0, int kb0, int kb1, float* lg,
                              int ld) {
   const int etiles = (E + 15) >> 4;
@@ -355,13 +380,20 @@ __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     lds[(i / ep) * ld + i % ep] = s;
   }
   __syncthreads();
-  router_tail_dispatch(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist,
-                       blk_rank);
-  if (!fd.counts || nblk != 1) return;
-  __syncthreads();  // the workgroup's own global writes are visible to it after the barrier
-  dispatch_body(idx_out, blk_hist, blk_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts,
-                fd.offsets, fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down,
-                fd.cd);
+  if (!fd.counts || nblk != 1) {
+    router_tail_dispatch(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist,
+                         blk_rank);
+    return;
+  }
+  // Fused dispatch (one token block, t0 = 0): the block's expert ids (sel,
+  // in pair order), histogram and ranks stay in LDS for the dispatch instead
+  // of a round trip through global memory.
+  __shared__ int32_t f_hist[kMaxExperts];
+  __shared__ int32_t f_rank[kRouterTokens * kMaxTopK];
+  router_tail_to(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, f_hist, f_rank);
+  __syncthreads();
+  dispatch_body(sel, f_hist, f_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts, fd.offsets,
+                fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down, fd.cd);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
