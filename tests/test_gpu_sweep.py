@@ -1,4 +1,4 @@
-"""GPU parity on a seeded sweep of random small layers: shapes, expert counts,
+"""GPU parity on a seeded sweep of random layers: shapes, expert counts,
 top-k, shared experts, token counts (including a single token and counts
 just past a tile or token block), both expert paths, the router options and
 MXFP4 experts, each against the fp64 oracle on the same inputs.
@@ -23,7 +23,7 @@ import torch
 import oracle
 import sparse_mixture_experts_histogram_amd as moe
 from cases import Options, custom, make_case
-from gpu_util import TOL, check_routing, rel_err, upload
+from gpu_util import TOL, check_routing, rel_err, sample_tokens, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,40 @@ def test_sweep_mxfp4(cfg):
     err = rel_err(y.cpu().numpy(), ref.y)
     print(f"{cfg.name}: max|err|/rms = {err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+def _draw_medium(n: int, seed: int):
+    """Larger layers (256-row prefill tiles, several token blocks, the wide
+    router when E * d >= 2^19), y checked on a sample of tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([4, 8, 16, 64, 160]))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        n_sh = int(rng.choice([0, 1]))
+        cfg = custom(f"medsweep{i}", 500 + i, T=int(rng.integers(300, 3000)),
+                     d=64 * int(rng.integers(4, 65)), E=E, k=k,
+                     ffn=64 * int(rng.integers(2, 33)), n_shared=n_sh,
+                     ffn_shared=64 * int(rng.integers(2, 17)) if n_sh else 0,
+                     bias="normal" if rng.random() < 0.4 else "none", bias_var=0.5)
+        scoring = "sigmoid" if rng.random() < 0.3 else "softmax"
+        out.append((cfg, Options(scoring=scoring), str(rng.choice(["auto", "prefill"]))))
+    return out
+
+
+MED_SWEEP = _draw_medium(8, 11)
+
+
+@pytest.mark.parametrize("item", MED_SWEEP, ids=[_id(s) for s in MED_SWEEP])
+def test_sweep_medium(item):
+    cfg, opts, path = item
+    c = make_case(cfg, opts=opts)
+    x, W = upload(c)
+    ref = c.oracle(sample_tokens(cfg.T))
+    y, idx, w, counts = moe.moe_forward(x, W, cfg.k, path=path, return_routing=True,
+                                        routing=moe.Routing(scoring=opts.scoring))
+    torch.cuda.synchronize()
+    check_routing(idx, w, counts, ref)
+    err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
+    print(f"{_id(item)}: max|err|/rms = {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
