@@ -22,6 +22,7 @@ __global__ __launch_bounds__(kDispatchThreads) void tiles_kernel(const int32_t* 
   __shared__ int gsize[kMaxGroups];
   __shared__ int mb_up[kMaxGroups + 1];
   __shared__ int mb_dn[kMaxGroups + 1];
+  __shared__ int rt_tab[kRowTileTable];
   const int tid = threadIdx.x;
   if (tid <= G) goff[tid] = offsets[tid];
   __syncthreads();
@@ -33,8 +34,8 @@ __global__ __launch_bounds__(kDispatchThreads) void tiles_kernel(const int32_t* 
   const int exd = block_excl_scan(tid < G ? (sz + cd.bm - 1) / cd.bm : 0, scan_buf, &mtot_d);
   if (tid <= G) mb_dn[tid] = tid < G ? exd : mtot_d;
   __syncthreads();
-  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up);
-  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down);
+  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab);
+  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab);
 }
 
 hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,

@@ -73,21 +73,34 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
 // (row tile fastest), so the workgroups that run together on one XCD share
 // both the weight tiles and the token tiles through that XCD's L2.
 // tiles[0] = {entry count, row tiles, column tiles, 0}.
+// The group of each row-tile slot is found once per slot (binary search over
+// the group bases) into the LDS table rt_tab when there are at most
+// kRowTileTable slots; entries then look it up.  (A search per entry was the
+// largest part of the dispatch for layers with many experts and tiles.)
+constexpr int kRowTileTable = 4096;
+__device__ __forceinline__ int group_of_slot(const int* mbase, int G, int mL) {
+  int lo = 0, hi = G - 1;  // largest g with mbase[g] <= mL (a non-empty group)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mbase[mid] <= mL) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
-                            TileCfg c, Tile* tiles) {
+                            TileCfg c, Tile* tiles, int* rt_tab) {
   const int total = mtot * c.n_tiles;
   if (threadIdx.x == 0) tiles[0] = Tile{total, mtot, c.n_tiles, 0};
+  const bool tab = mtot <= kRowTileTable;
+  if (tab) {
+    for (int m = threadIdx.x; m < mtot; m += blockDim.x) rt_tab[m] = group_of_slot(mbase, G, m);
+    __syncthreads();
+  }
   // Row-tile list only: entry 1 + i is row tile i (in group order); a kernel
   // reads entry L as row tile L % mtot of column tile L / mtot.
   const int entries = c.row_list ? mtot : total;
   for (int L = threadIdx.x; L < entries; L += blockDim.x) {
     const int mL = c.row_list ? L : L / c.n_tiles;  // row tile "slot"
-    int lo = 0, hi = G - 1;  // largest g with mbase[g] <= mL (a non-empty group)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (mbase[mid] <= mL) lo = mid; else hi = mid - 1;
-    }
-    const int g = lo;
+    const int g = tab ? rt_tab[mL] : group_of_slot(mbase, G, mL);
     if (c.row_list) {
       const int m0 = goff[g] + (mL - mbase[g]) * c.bm;
       tiles[1 + L] = Tile{g, m0, min(m0 + c.bm, goff[g] + gsize[g]), 0};
@@ -105,6 +118,7 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
     const int mend = min(m0 + c.bm, goff[g] + gsize[g]);
     tiles[1 + L] = Tile{g, m0, mend, nt * c.bn};
   }
+  if (tab) __syncthreads();  // the table is free again
 }
 
 // The whole dispatch, run by one workgroup of kDispatchThreads threads.
@@ -121,6 +135,7 @@ __device__ __forceinline__ void dispatch_body(
   __shared__ int gsize[kMaxGroups];
   __shared__ int mb_up[kMaxGroups + 1];
   __shared__ int mb_dn[kMaxGroups + 1];
+  __shared__ int rt_tab[kRowTileTable];
   const int tid = threadIdx.x;
   const int G = E + n_sh;
 
@@ -129,7 +144,7 @@ __device__ __forceinline__ void dispatch_body(
   // thread each; a thread per expert then walks the S segment sums in order.
   // (S is not simply kDispatchThreads / Ep: with few blocks that serial walk
   // over mostly empty segments was most of the dispatch time.)
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
   const int S = min(kDispatchThreads / Ep, max(1, (nblk + kBatch - 1) / kBatch));
@@ -194,8 +209,8 @@ __device__ __forceinline__ void dispatch_body(
   if (tid <= G) mb_dn[tid] = tid < G ? exd : mtot_d;
   __syncthreads();
   for (int g = tid; g <= G; g += blockDim.x) offsets[g] = goff[g];
-  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up);
-  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down);
+  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab);
+  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab);
 
   // 4. stable placement of the routed pairs, kPlace pairs per thread at a
   // time (their index and rank loads, then their block-offset loads, are
