@@ -49,6 +49,10 @@ SMALL = {c.name: c for c in [
     # many tokens and a large router matrix (E * d >= 2^19): the wide router
     # (64-token workgroups over K parts); T not a multiple of 64
     custom("wide_router", 116, T=300, d=4096, E=128, k=4, ffn=64, bias="normal", bias_var=0.5),
+    # 128-row prefill tiles with skewed loads (two experts over 500 rows,
+    # one with 2) and a shared expert of 1200 rows
+    custom("split_tiles", 117, T=1200, d=256, E=16, k=2, ffn=192, n_shared=1, ffn_shared=320,
+           bias="normal", bias_var=0.5),
     NAMED["tiny_f32"],
 ]}
 
