@@ -355,8 +355,8 @@ struct FusedDispatch {
 // partial loads of an element are issued before the first add, so the sum
 // costs one memory round trip.  With a single token block and fd.counts
 // set, the one workgroup then runs the whole dispatch (dispatch_body.h) on
-// the indices, histogram and ranks it has just written, which saves the
-// dispatch launch.  (With several blocks that would take a device-scope
+// the indices, histogram and ranks it has just computed (kept in LDS), which
+// saves the dispatch launch.  (With several blocks that would take a device-scope
 // fence, which writes back and invalidates L2 and measured slower than the
 // separate launch.)  kDispatchThreads threads; dynamic LDS: [16][ld] floats,
 // then sel[16*k].
