@@ -345,7 +345,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
-              "(multi-GPU expert parallelism is not part of this build)", file=sys.stderr)
+              "(multi-GPU expert parallelism is not implemented; the library runs one GPU)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

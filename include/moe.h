@@ -87,7 +87,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* a size, pointer or enum is out of range        */
-  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape this build rejects    */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape the kernels reject    */
   MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than needed  */
   MOE_ERR_HIP = -4          /* a HIP call or kernel launch failed             */
 } moe_status;

@@ -212,7 +212,7 @@ const char* moe_status_str(int s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: argument out of range";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by the kernels";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
     default: return "unknown moe_status";
