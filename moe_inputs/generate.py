@@ -39,9 +39,13 @@ from .configs import MoEConfig
 # stream ids
 X, W_ROUTER, W_UP, W_GATE, W_DOWN, WS_UP, WS_GATE, WS_DOWN, BIAS = range(9)
 MX_UP, MX_GATE, MX_DOWN = range(9, 12)
+MX8_UP, MX8_GATE, MX8_DOWN = range(12, 15)
 # rms of the E2M1 values when all 16 codes are equally likely: the values are
 # 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, sqrt(68.5 / 8)
 _E2M1_RMS = 2.9261
+# rms of the E4M3 values when the 254 non-NaN codes are equally likely
+# (a log-spread from 2^-9 to 448, so the large codes dominate)
+_E4M3_RMS = 100.0577
 
 
 def _rng(cfg: MoEConfig, tensor_id: int, expert_id: int = 0) -> np.random.Generator:
@@ -180,4 +184,45 @@ def stacked_mxfp4(cfg: MoEConfig, shared: bool = False):
     for e in range(n):
         (up[e], up_s[e]), (gate[e], gate_s[e]), (down[e], down_s[e]) = \
             mxfp4_expert_weights(cfg, e, shared)
+    return up, up_s, gate, gate_s, down, down_s
+
+
+def _mx8_draw(cfg: MoEConfig, tensor_id: int, expert_id: int, rows: int, cols: int,
+              std: float) -> Tuple[np.ndarray, np.ndarray]:
+    """(codes [rows, cols] uint8, scales [rows, cols/32] uint8) of one MXFP8
+    (E4M3) matrix whose values have an rms within a factor of two of
+    ``std``; the two NaN codes are never drawn."""
+    rng = _rng(cfg, tensor_id, expert_id)
+    codes = rng.integers(0, 254, size=(rows, cols), dtype=np.uint8)
+    codes = codes + (codes >= 0x7F) + (codes >= 0xFE)  # skip 0x7F and 0xFF
+    base = int(round(127 + np.log2(std / _E4M3_RMS)))
+    scales = (base + rng.integers(-1, 2, size=(rows, cols // 32))).astype(np.uint8)
+    return codes.astype(np.uint8), scales
+
+
+def mxfp8_expert_weights(cfg: MoEConfig, e: int, shared: bool = False):
+    """((up codes, up scales), (gate codes, gate scales), (down codes, down
+    scales)) of routed expert e (or shared expert e) stored as MXFP8."""
+    f = cfg.ffn_shared if shared else cfg.ffn
+    sd_in, sd_mid = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(f)
+    sid = 1000 + e if shared else e
+    return (_mx8_draw(cfg, MX8_UP, sid, f, cfg.d, sd_in),
+            _mx8_draw(cfg, MX8_GATE, sid, f, cfg.d, sd_in),
+            _mx8_draw(cfg, MX8_DOWN, sid, cfg.d, f, sd_mid))
+
+
+def stacked_mxfp8(cfg: MoEConfig, shared: bool = False):
+    """All routed (or shared) MXFP8 experts stacked: (up, up_scale, gate,
+    gate_scale, down, down_scale) uint8 arrays."""
+    n = cfg.n_shared if shared else cfg.E
+    f = cfg.ffn_shared if shared else cfg.ffn
+    up = np.empty((n, f, cfg.d), np.uint8)
+    up_s = np.empty((n, f, cfg.d // 32), np.uint8)
+    gate = np.empty_like(up)
+    gate_s = np.empty_like(up_s)
+    down = np.empty((n, cfg.d, f), np.uint8)
+    down_s = np.empty((n, cfg.d, f // 32), np.uint8)
+    for e in range(n):
+        (up[e], up_s[e]), (gate[e], gate_s[e]), (down[e], down_s[e]) = \
+            mxfp8_expert_weights(cfg, e, shared)
     return up, up_s, gate, gate_s, down, down_s

@@ -12,5 +12,5 @@ from .moe import (  # noqa: F401
     widen, router_logits, softmax, select_topk, renormalise, route, expert_counts,
     dispatch_order, silu, swiglu_expert, moe_forward, topk_gaps, share_touched,
     sigmoid, kept_scores, selection_keys, expert_capacity, capacity_keep, e2m1_value,
-    e8m0_value, dequant_mxfp4, widen_weight, MoEResult,
+    e8m0_value, dequant_mxfp4, e4m3_value, dequant_mxfp8, widen_weight, MoEResult,
 )

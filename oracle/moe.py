@@ -59,7 +59,10 @@ consecutive elements along K share one E8M0 scale 2^(S-127); each element is
 FP4 E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; exponent 0 is
 subnormal: 0 or 0.5).  Two elements per byte, element 2i in the low nibble.
 The layer computes with the dequantized weights exactly as with stored
-bf16/f32 weights.
+bf16/f32 weights.  For the 8-bit expert weights the pages mention (P3 "What
+mixture of experts costs in memory": DeepSeek-V3's weights are mostly 8-bit)
+the same MX blocking is used with FP8 E4M3 elements (MXFP8: bias 7, no
+infinity, 0x7F/0xFF NaN), one element per byte.
 
 Parity status: every function here is pinned by a CPU test against the pages'
 printed worked example, closed forms, brute force or a library routine, except
@@ -117,11 +120,38 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (el.reshape(N, K // 32, 32) * sc[:, :, None]).reshape(N, K)
 
 
+def e4m3_value(code: int) -> float:
+    """Value of an 8-bit E4M3 code (OCP FP8, the element of MXFP8): sign,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal
+    (2^-6 * m/8); 0x7F and 0xFF (exponent and mantissa all ones) are NaN and
+    there is no infinity, so the largest magnitude is 1.75 * 2^8 = 448."""
+    s, e, m = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = 2.0 ** -6 * (m / 8.0) if e == 0 else 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return -mag if s else mag
+
+
+def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 (E4M3 elements) matrix -> float64.  codes [N, K] uint8, scales
+    [N, K/32] uint8 -> [N, K] = element * scale of its 32-element block."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    N, K = codes.shape
+    if scales.shape != (N, K // 32) or K % 32:
+        raise ValueError("MXFP8 shapes")
+    table = np.array([e4m3_value(c) for c in range(256)])
+    sc = np.array([e8m0_value(b) for b in range(256)])[scales]
+    return (table[codes].reshape(N, K // 32, 32) * sc[:, :, None]).reshape(N, K)
+
+
 def widen_weight(w, dtype: str) -> np.ndarray:
-    """A stored weight matrix -> float64: a bf16/f32 array, or for 'mxfp4'
-    a (codes, scales) pair."""
+    """A stored weight matrix -> float64: a bf16/f32 array, or for 'mxfp4' /
+    'mxfp8' a (codes, scales) pair."""
     if dtype == "mxfp4":
         return dequant_mxfp4(*w)
+    if dtype == "mxfp8":
+        return dequant_mxfp8(*w)
     return widen(w, dtype)
 
 

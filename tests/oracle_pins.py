@@ -472,10 +472,80 @@ def check_mxfp4_layer_bruteforce(seed=28, T=12, d=64, E=4, k=2, f=32):
     assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
 
 
+# ---------------------------------------------------------------- MXFP8 expert weights
+def check_e4m3_library():
+    """All 256 E4M3 codes against torch's float8_e4m3fn conversion (NaN at
+    0x7F and 0xFF, no infinity)."""
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([om.e4m3_value(v) for v in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def check_e4m3_closed_forms():
+    """Codes whose values the format fixes: 0x38 = 1 (exponent field 7 =
+    bias), 0xB8 = -1, 0x7E = 1.75 * 2^8 = 448 (the largest), 0x08 = 2^-6
+    (the smallest normal), 0x01 = 2^-9 (the smallest subnormal), 0x00 = 0."""
+    for code, v in [(0x38, 1.0), (0xB8, -1.0), (0x7E, 448.0), (0x08, 2.0 ** -6),
+                    (0x01, 2.0 ** -9), (0x00, 0.0), (0x3C, 1.5), (0x40, 2.0)]:
+        assert om.e4m3_value(code) == v, (hex(code), om.e4m3_value(code))
+    assert math.isnan(om.e4m3_value(0x7F)) and math.isnan(om.e4m3_value(0xFF))
+
+
+def check_mxfp8_dequant(seed=29):
+    """Dequantisation against torch's E4M3 values element by element, each
+    times the E8M0 scale of its 32-element block, and a hand-made row."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(4, 96), dtype=np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    scales = rng.integers(110, 140, size=(4, 3), dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    ref = ref * 2.0 ** (scales.astype(np.int64)[:, np.arange(96) // 32] - 127)
+    assert np.array_equal(om.dequant_mxfp8(codes, scales), ref)
+    row = np.full((1, 64), 0x38, dtype=np.uint8)
+    d = om.dequant_mxfp8(row, np.array([[127, 130]], dtype=np.uint8))[0]
+    assert d[:32].tolist() == [1.0] * 32 and d[32:].tolist() == [8.0] * 32
+
+
+def check_mxfp8_layer_bruteforce(seed=30, T=10, d=64, E=3, k=2, f=32):
+    """The layer with MXFP8 experts equals a dense evaluation on torch's
+    E4M3 values times the block scales."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / np.sqrt(d)
+
+    def draw(r, c):
+        codes = rng.integers(0, 256, size=(r, c), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x30
+        return codes, rng.integers(118, 124, size=(r, c // 32), dtype=np.uint8)
+
+    mx = [tuple(draw(r, c) for r, c in ((f, d), (f, d), (d, f))) for _ in range(E)]
+    r = om.moe_forward(x, wr, None, k, lambda e: mx[e], E, "f32", expert_dtype="mxfp8")
+
+    def dense(codes, scales):
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+        return v * 2.0 ** (scales.astype(np.int64)[:, np.arange(codes.shape[1]) // 32] - 127)
+
+    P = scipy.special.softmax(x @ wr.T, axis=1)
+    y = np.zeros((T, d))
+    for t in range(T):
+        best = sorted(max(itertools.combinations(range(E), k),
+                          key=lambda c: sum((x @ wr.T)[t, list(c)])))
+        g = P[t, best] / P[t, best].sum()
+        for j, e in enumerate(best):
+            y[t] += g[j] * torch_ffn(x[t], *(dense(*m) for m in mx[e]))[0]
+    assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
+
+
 ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, check_tie_break,
        check_softmax_library, check_invariants, check_uniform_gates,
        check_single_expert_library, check_silu, check_widen, check_occupancy_table,
        check_occupancy_monte_carlo, check_sigmoid_library, check_sigmoid_bias_selection_only,
        check_sigmoid_routing_bruteforce, check_raw_softmax_weights, check_capacity_closed_forms,
        check_capacity_bruteforce, check_sigmoid_layer_bruteforce, check_e2m1_table,
-       check_e8m0_library, check_mxfp4_dequant, check_mxfp4_layer_bruteforce]
+       check_e8m0_library, check_mxfp4_dequant, check_mxfp4_layer_bruteforce,
+       check_e4m3_library, check_e4m3_closed_forms, check_mxfp8_dequant,
+       check_mxfp8_layer_bruteforce]

@@ -89,3 +89,24 @@ def test_config_shapes_match_page_parameter_counts():
     exp_B = G["mixtral_layers"] * mx.E * mx.expert_params() / 1e9
     other = G["mixtral_total_B"] - exp_B
     assert round(other + exp_B * mx.k / mx.E, 1) == G["mixtral_active_B"]
+
+
+def test_mx_weight_recipes():
+    """MXFP4 and MXFP8 test weights: shapes, no NaN codes (MXFP8), a
+    deterministic stream, and an rms within a factor of two of the dense
+    recipe's 1/sqrt(fan_in)."""
+    import oracle
+    from moe_inputs import NAMED, generate
+    cfg = NAMED["gpt_oss"]
+    for fmt, draw, deq in (("mxfp4", generate.mxfp4_expert_weights, oracle.dequant_mxfp4),
+                           ("mxfp8", generate.mxfp8_expert_weights, oracle.dequant_mxfp8)):
+        (u, us), _, (d, ds) = draw(cfg, 3)
+        assert u.shape == (cfg.ffn, cfg.d // (2 if fmt == "mxfp4" else 1)), fmt
+        assert us.shape == (cfg.ffn, cfg.d // 32) and ds.shape == (cfg.d, cfg.ffn // 32)
+        if fmt == "mxfp8":
+            assert not np.isin(u, [0x7F, 0xFF]).any() and not np.isin(d, [0x7F, 0xFF]).any()
+        (u2, _), _, _ = draw(cfg, 3)
+        assert np.array_equal(u, u2)
+        rms = float(np.sqrt(np.mean(deq(u, us) ** 2)))
+        target = 1.0 / np.sqrt(cfg.d)
+        assert target / 2 <= rms <= 2 * target, (fmt, rms, target)

@@ -105,12 +105,42 @@ def _dequant_block16(codes, scales):
 
 _REAL_DEQUANT = om.dequant_mxfp4
 
+
+def _e4m3_bias8(code):
+    s, e, m = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = 2.0 ** -7 * (m / 8.0) if e == 0 else 2.0 ** (e - 8) * (1.0 + m / 8.0)
+    return -mag if s else mag
+
+
+def _e4m3_no_subnormals(code):
+    s, e, m = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = 0.0 if e == 0 else 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return -mag if s else mag
+
+
+def _dequant8_block16(codes, scales):
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    table = np.array([om.e4m3_value(c) for c in range(256)])
+    nb = np.asarray(scales).shape[1]
+    sc = 2.0 ** (np.asarray(scales, np.int64)[:, (np.arange(K) // 16) % nb] - 127)
+    return table[codes] * sc
+
 MUTANTS = [
     ("e2m1_value", _e2m1_bias2, P.check_e2m1_table),
     ("e8m0_value", _e8m0_bias128, P.check_e8m0_library),
     ("dequant_mxfp4", _dequant_high_nibble_first, P.check_mxfp4_dequant),
     ("dequant_mxfp4", _dequant_block16, P.check_mxfp4_dequant),
     ("dequant_mxfp4", _dequant_high_nibble_first, P.check_mxfp4_layer_bruteforce),
+    ("e4m3_value", _e4m3_bias8, P.check_e4m3_library),
+    ("e4m3_value", _e4m3_bias8, P.check_e4m3_closed_forms),
+    ("e4m3_value", _e4m3_no_subnormals, P.check_e4m3_library),
+    ("dequant_mxfp8", _dequant8_block16, P.check_mxfp8_dequant),
+    ("dequant_mxfp8", _dequant8_block16, P.check_mxfp8_layer_bruteforce),
     ("selection_keys", _sigmoid_of_biased_logit, P.check_sigmoid_bias_selection_only),
     ("sigmoid", _sign_sigmoid, P.check_sigmoid_library),
     ("sigmoid", _sign_sigmoid, P.check_sigmoid_routing_bruteforce),
