@@ -51,8 +51,8 @@ def parse():
     ap.add_argument("--variants", action="store_true",
                     help="also time the router options: sigmoid / raw routing on the "
                          "DeepSeek-V3-shaped router, capacity cuts on the Mixtral-shaped "
-                         "layer, and MXFP4 experts on the gpt-oss-shaped decode layer "
-                         "(reported under \"variants\")")
+                         "layer, and MXFP4 and MXFP8 experts on the gpt-oss-shaped decode "
+                         "layer (reported under \"variants\")")
     return ap.parse_args()
 
 
@@ -238,15 +238,16 @@ def time_variants(cfg, x, W, k, steps):
         del wsm
     out["capacity_mixtral_t4096"] = cap_out
     out["mxfp4_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128], 50)
+    out["mxfp8_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128], 50, fmt="mxfp8")
     return out
 
 
-def time_mx_decode(Ts, iters):
+def time_mx_decode(Ts, iters, fmt="mxfp4"):
     """The gpt-oss-shaped layer (d=2880, 128 experts, top-4, ffn 2880) with
-    MXFP4 expert weights at decode batch sizes: per-iteration hipEvents before
-    the first and after the last launch, L2 and MALL flushed by a 1 GiB read
-    between iterations, median of `iters`; HBM fraction on the touched
-    experts' code and scale bytes."""
+    MXFP4 (or, fmt="mxfp8", MXFP8) expert weights at decode batch sizes:
+    per-iteration hipEvents before the first and after the last launch, L2
+    and MALL flushed by a 1 GiB read between iterations, median of `iters`;
+    HBM fraction on the touched experts' code and scale bytes."""
     import ctypes
     import numpy as np
     import torch
@@ -256,7 +257,8 @@ def time_mx_decode(Ts, iters):
 
     cfg = NAMED["gpt_oss"]
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    u, us, g, gs, dn, ds = generate.stacked_mxfp4(cfg)
+    stack = generate.stacked_mxfp4 if fmt == "mxfp4" else generate.stacked_mxfp8
+    u, us, g, gs, dn, ds = stack(cfg)
     li = tables.layer_inputs(cfg, max(Ts))
     W = moe.MxWeights(w_router=torch.from_numpy(li.w_router.view(np.int16)).view(torch.bfloat16).cuda(),
                       up=t(u), up_scale=t(us), gate=t(g), gate_scale=t(gs), down=t(dn),
@@ -265,7 +267,7 @@ def time_mx_decode(Ts, iters):
     xall = torch.from_numpy(li.x.view(np.int16)).view(torch.bfloat16).cuda()
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
     flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
-    per_expert = 3 * cfg.d * cfg.ffn * (0.5 + 1.0 / 32)
+    per_expert = 3 * cfg.d * cfg.ffn * ((0.5 if fmt == "mxfp4" else 1.0) + 1.0 / 32)
     res = {}
     for T in Ts:
         x = xall[:T].contiguous()

@@ -51,6 +51,11 @@
  *    types; products use the exactly dequantised weights.  Such a layer is
  *    run with moe_forward_mx, which also takes the scale arrays; it always
  *    uses the streaming (decode) expert kernels, whatever `path` says.
+ *  - expert_format = MOE_EXPERTS_MXFP8 (page "Mixture of experts: how MoE
+ *    works and what it costs", "What mixture of experts costs in memory":
+ *    8-bit expert weights): the same MX blocking with FP8 E4M3 elements
+ *    (bias 7, no infinity, 0x7F/0xFF NaN), one per byte.  d and ffn (and
+ *    ffn_shared) at most 8192 (MOE_ERR_UNSUPPORTED otherwise).
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
@@ -104,7 +109,11 @@ typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } mo
 typedef enum moe_weighting { MOE_WEIGHTS_RENORM = 0, MOE_WEIGHTS_RAW = 1 } moe_weighting;
 
 /* Storage of the expert weights: `dtype`, or MXFP4 (see the options above). */
-typedef enum moe_expert_format { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1 } moe_expert_format;
+typedef enum moe_expert_format {
+  MOE_EXPERTS_DENSE = 0,
+  MOE_EXPERTS_MXFP4 = 1,
+  MOE_EXPERTS_MXFP8 = 2
+} moe_expert_format;
 
 typedef struct moe_desc {
   int64_t T;          /* tokens, >= 0                                        */
@@ -197,7 +206,8 @@ typedef struct moe_mx_scales {
  * moe_forward for a layer with expert_format MOE_EXPERTS_MXFP4: w_up, w_gate
  * [E,ffn,d/2], w_down [E,d,ffn/2] (and the shared counterparts) hold the
  * packed E2M1 codes, `scales` their E8M0 scales (16-byte aligned like the
- * codes).  Every other argument is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
+ * codes).  With MOE_EXPERTS_MXFP8 the code arrays hold one E4M3 byte per
+ * element: w_up, w_gate [E,ffn,d], w_down [E,d,ffn].  Every other argument is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
  * moe_forward_timed.  Scale bytes 0 (2^-127) and 255 (NaN) follow the format
  * but results that leave bfloat16's normal range are not defined.
  */

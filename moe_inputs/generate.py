@@ -43,9 +43,12 @@ MX8_UP, MX8_GATE, MX8_DOWN = range(12, 15)
 # rms of the E2M1 values when all 16 codes are equally likely: the values are
 # 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, sqrt(68.5 / 8)
 _E2M1_RMS = 2.9261
-# rms of the E4M3 values when the 254 non-NaN codes are equally likely
-# (a log-spread from 2^-9 to 448, so the large codes dominate)
-_E4M3_RMS = 100.0577
+# MXFP8 test codes: any sign and mantissa, exponent field 4..9 (magnitudes
+# 2^-3 .. 7.5, a spread like that of E2M1's 0.5 .. 6; codes over the whole
+# E4M3 range would span 2^-9 .. 448 and let a few weights dominate); rms of
+# those 96 equally likely values
+_E4M3_EXP_LO, _E4M3_EXP_HI = 4, 9
+_E4M3_RMS = 2.7635
 
 
 def _rng(cfg: MoEConfig, tensor_id: int, expert_id: int = 0) -> np.random.Generator:
@@ -191,10 +194,12 @@ def _mx8_draw(cfg: MoEConfig, tensor_id: int, expert_id: int, rows: int, cols: i
               std: float) -> Tuple[np.ndarray, np.ndarray]:
     """(codes [rows, cols] uint8, scales [rows, cols/32] uint8) of one MXFP8
     (E4M3) matrix whose values have an rms within a factor of two of
-    ``std``; the two NaN codes are never drawn."""
+    ``std`` (no NaN code can be drawn)."""
     rng = _rng(cfg, tensor_id, expert_id)
-    codes = rng.integers(0, 254, size=(rows, cols), dtype=np.uint8)
-    codes = codes + (codes >= 0x7F) + (codes >= 0xFE)  # skip 0x7F and 0xFF
+    sign = rng.integers(0, 2, size=(rows, cols), dtype=np.uint8)
+    expo = rng.integers(_E4M3_EXP_LO, _E4M3_EXP_HI + 1, size=(rows, cols), dtype=np.uint8)
+    mant = rng.integers(0, 8, size=(rows, cols), dtype=np.uint8)
+    codes = (sign << 7) | (expo << 3) | mant
     base = int(round(127 + np.log2(std / _E4M3_RMS)))
     scales = (base + rng.integers(-1, 2, size=(rows, cols // 32))).astype(np.uint8)
     return codes.astype(np.uint8), scales

@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 WEIGHTS_RENORM, WEIGHTS_RAW = 0, 1
-EXPERTS_DENSE, EXPERTS_MXFP4 = 0, 1
+EXPERTS_DENSE, EXPERTS_MXFP4, EXPERTS_MXFP8 = 0, 1, 2
 ABI_VERSION = 3
 
 

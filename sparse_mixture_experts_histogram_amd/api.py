@@ -33,12 +33,17 @@ class Routing:
 
 def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
               dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto",
-              routing: Routing = Routing(), mxfp4: bool = False) -> MoeDesc:
+              routing: Routing = Routing(), mxfp4: bool = False,
+              expert_format: Optional[str] = None) -> MoeDesc:
+    """Layer descriptor.  ``expert_format``: None / "dense", "mxfp4" or
+    "mxfp8" (``mxfp4=True`` is the same as "mxfp4")."""
+    fmt = expert_format or ("mxfp4" if mxfp4 else "dense")
     return MoeDesc(T=T, d=d, E=E, k=k, ffn=ffn, n_shared=n_shared,
                    ffn_shared=ffn_shared if n_shared else 0, dtype=_DT[dtype],
                    y_dtype=_DT[y_dtype], path=_PATHS[path], scoring=_SCORING[routing.scoring],
                    weighting=_lib.WEIGHTS_RENORM if routing.renormalize else _lib.WEIGHTS_RAW,
-                   expert_format=_lib.EXPERTS_MXFP4 if mxfp4 else _lib.EXPERTS_DENSE,
+                   expert_format={"dense": _lib.EXPERTS_DENSE, "mxfp4": _lib.EXPERTS_MXFP4,
+                                  "mxfp8": _lib.EXPERTS_MXFP8}[fmt],
                    flags=0, capacity_factor=float(routing.capacity_factor))
 
 
@@ -152,16 +157,17 @@ def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path
 
 @dataclass
 class MxWeights:
-    """A layer whose expert weights are MXFP4: uint8 E2M1 code tensors
-    (two codes per byte, element 2i in the low nibble) and uint8 E8M0 scale
-    tensors (one per 32 elements along K).  Router weight (bf16) and bias as
-    in ``Weights``."""
+    """A layer whose expert weights are MX-format: MXFP4 (uint8 E2M1 code
+    tensors, two codes per byte, element 2i in the low nibble) or MXFP8 (one
+    E4M3 code per byte), with uint8 E8M0 scale tensors (one per 32 elements
+    along K).  The format follows from the code tensors' last dimension.
+    Router weight (bf16) and bias as in ``Weights``."""
     w_router: torch.Tensor                 # [E, d] bf16
-    up: torch.Tensor                       # [E, ffn, d/2] uint8
+    up: torch.Tensor                       # [E, ffn, d/2] (MXFP4) or [E, ffn, d] (MXFP8) uint8
     up_scale: torch.Tensor                 # [E, ffn, d/32] uint8
     gate: torch.Tensor
     gate_scale: torch.Tensor
-    down: torch.Tensor                     # [E, d, ffn/2] uint8
+    down: torch.Tensor                     # [E, d, ffn/2] or [E, d, ffn] uint8
     down_scale: torch.Tensor               # [E, d, ffn/32] uint8
     bias: Optional[torch.Tensor] = None    # [E] float32
     s_up: Optional[torch.Tensor] = None    # shared experts, same layout with ffn_shared
@@ -171,21 +177,28 @@ class MxWeights:
     s_down: Optional[torch.Tensor] = None
     s_down_scale: Optional[torch.Tensor] = None
 
+    @property
+    def format(self) -> str:
+        d = self.up_scale.shape[2] * 32
+        return "mxfp8" if self.up.shape[2] == d else "mxfp4"
+
     def desc(self, T: int, k: int, y_dtype=torch.float32,
              routing: Routing = Routing()) -> MoeDesc:
-        E, ffn, half_d = self.up.shape
+        E, ffn, _ = self.up.shape
+        d = self.up_scale.shape[2] * 32
         ns = 0 if self.s_up is None else self.s_up.shape[0]
         fs = 0 if self.s_up is None else self.s_up.shape[1]
-        return make_desc(T, 2 * half_d, E, k, ffn, ns, fs, torch.bfloat16, y_dtype, "auto",
-                         routing, mxfp4=True)
+        return make_desc(T, d, E, k, ffn, ns, fs, torch.bfloat16, y_dtype, "auto",
+                         routing, expert_format=self.format)
 
 
 def _check_mx(W: MxWeights, x: torch.Tensor):
-    E, ffn, half_d = W.up.shape
-    d = 2 * half_d
+    E, ffn, _ = W.up.shape
+    d = W.up_scale.shape[2] * 32
+    per = 2 if W.format == "mxfp4" else 1   # codes per byte
     if x.dtype != torch.bfloat16 or W.w_router.dtype != torch.bfloat16:
-        raise ValueError("MXFP4 layers take bf16 x and router weight")
-    want = {"up": (E, ffn, d // 2), "gate": (E, ffn, d // 2), "down": (E, d, ffn // 2),
+        raise ValueError("MX-format layers take bf16 x and router weight")
+    want = {"up": (E, ffn, d // per), "gate": (E, ffn, d // per), "down": (E, d, ffn // per),
             "up_scale": (E, ffn, d // 32), "gate_scale": (E, ffn, d // 32),
             "down_scale": (E, d, ffn // 32)}
     for name, shape in want.items():
@@ -201,7 +214,7 @@ def _check_mx(W: MxWeights, x: torch.Tensor):
 def moe_forward_mx(x: torch.Tensor, W: MxWeights, k: int, y_dtype=torch.float32,
                    ws: Optional[torch.Tensor] = None, return_routing: bool = False,
                    routing: Routing = Routing(), events=None, y: Optional[torch.Tensor] = None):
-    """y = MoE(x) with MXFP4 expert weights.  With return_routing, also
+    """y = MoE(x) with MX-format (MXFP4 or MXFP8) expert weights.  With return_routing, also
     (topk_idx, topk_w, expert_counts).  ``events``: a void** of 6 hipEvents
     (see moe_forward_timed) or None; ``y``: a preallocated output."""
     _check_mx(W, x)

@@ -64,7 +64,7 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
                  const moe_mx_scales* mx, void* y, int32_t* topk_idx, float* topk_w,
                  int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                  moe_stream stream, void* const* events) {
-  if (d && (d->expert_format == MOE_EXPERTS_MXFP4) != (mx != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (d && (d->expert_format != MOE_EXPERTS_DENSE) != (mx != nullptr)) return MOE_ERR_INVALID_ARG;
   Plan P;
   bool empty = false;
   int st = prepare(d, workspace, workspace_bytes, &P, &empty);

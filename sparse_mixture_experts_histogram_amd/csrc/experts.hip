@@ -761,15 +761,24 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
 // reads spread over the banks.  Blocks past K copy a clamped chunk and
 // their codes are zeroed; waves past N (a partial tile) re-read the last
 // row and store nothing.  Needs K a multiple of 64 and at most kMxLdsMaxK.
-template <bool UPGATE, int NW>
+// EB = 8 is the MXFP8 form: E4M3 codes, one per byte, so a row's stage is
+// 256 bytes (a copy moves 4 rows, chunk c of row r at slot c ^ r % 16), a
+// lane reads 8 bytes of its block and widens them with
+// v_cvt_scalef32_pk_bf16_fp8; K up to kMx8MaxK.
+template <bool UPGATE, int NW, int EB>
 __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   constexpr int NS = UPGATE ? 2 : 1;
   constexpr int XS = 16 * 256;               // token stage, bf16 elements (8 KB)
   constexpr int XI = 8 / NW;                 // token copies per wave and stage
-  constexpr int CS = NW * NS * 2048;         // code stage, bytes (2 KB per wave and matrix)
-  constexpr int SCS = 16 * NW * (kMxLdsMaxK / 32);  // scales of one matrix, bytes
-  constexpr int NLD = XI + 2 * NS;           // copies per wave and stage
+  constexpr int RB = 32 * EB;                // code bytes of a row per stage (128 / 256)
+  constexpr int CS = NW * NS * 16 * RB;      // code stage, bytes
+  constexpr int NCC = 16 * RB / 1024;        // code copies per wave, matrix and stage
+  constexpr int RPC = 1024 / RB, LPR = RB / 16;  // rows per copy, lanes per row
+  constexpr int KMAX = EB == 8 ? kMx8MaxK : kMxLdsMaxK;
+  constexpr int SCS = 16 * NW * (KMAX / 32);  // scales of one matrix, bytes
+  constexpr int NLD = XI + NCC * NS;         // copies per wave and stage
   static_assert(NW == 4 || NW == 8, "the token slab splits into 1 KB copies per wave");
+  static_assert(EB == 4 || EB == 8, "FP4 or FP8 elements");
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
   const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
@@ -782,7 +791,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   const int ge = sh ? tl.g - a.E : tl.g;
   const int nb = K >> 5;                 // 32-k blocks
   const int nst = (nb + 7) >> 3;         // 256-k stages
-  const int64_t cstride = (int64_t)N * (K / 2), sstride = (int64_t)N * nb;
+  const int rowb = K * EB / 8;           // code bytes per weight row
+  const int64_t cstride = (int64_t)N * rowb, sstride = (int64_t)N * nb;
   // one named array per stage, so the compiler tells reads of one stage
   // from copies still landing in another
   __shared__ __attribute__((aligned(1024))) uint16_t lx0[XS], lx1[XS], lx2[XS];
@@ -804,20 +814,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
     xsrc[i] = a.tok + xtok * a.ldt;
     xchunk[i] = (lane & 31) ^ (xr & 15);
   }
-  // code copy: instruction i of a matrix holds feature rows 16 w + 8 i + l / 8;
-  // lane l takes slot l % 8, global chunk (32-k block of the stage) slot ^ (row / 2) % 8
-  const uint8_t* csrc[NS][2];
-  int cchunk[2];
+  // code copy: instruction i of a matrix holds feature rows 16 w + RPC i +
+  // l / LPR; lane l takes slot l % LPR, the row's 16-byte chunk of the stage
+  // slot ^ (row / 2) % 8 (FP4) or slot ^ row % 16 (FP8)
+  const uint8_t* csrc[NS][NCC];
+  int cchunk[NCC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int cr = 8 * i + (lane >> 3);
-    cchunk[i] = (lane & 7) ^ ((cr >> 1) & 7);
+  for (int i = 0; i < NCC; ++i) {
+    const int cr = RPC * i + lane / LPR;
+    cchunk[i] = (lane % LPR) ^ (EB == 4 ? ((cr >> 1) & 7) : (cr & 15));
     int64_t cn = tl.n0 + 16 * wave + cr;
     cn = cn < N ? cn : N - 1;
 #pragma unroll
     for (int q = 0; q < NS; ++q)
       csrc[q][i] = (const uint8_t*)(q == 0 ? (sh ? a.s0 : a.w0) : (sh ? a.s1 : a.w1)) +
-                   ge * cstride + cn * (K / 2);
+                   ge * cstride + cn * rowb;
   }
   // the row lookups above have landed before any copy is issued (a load
   // into registers behind copies in flight would wait for all of them)
@@ -853,11 +864,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < NS; ++q)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int b = 8 * st + cchunk[i];          // 32-k block = 16-byte code chunk
-        b = b < nb ? b : nb - 1;
+      for (int i = 0; i < NCC; ++i) {
+        int b = LPR * st + cchunk[i];        // 16-byte code chunk along the row
+        b = b < rowb / 16 ? b : rowb / 16 - 1;
         __builtin_amdgcn_global_load_lds((const void*)(csrc[q][i] + b * 16),
-                                         LDS_PTR(lc + (wave * NS + q) * 2048 + i * 1024), 16,
+                                         LDS_PTR(lc + (wave * NS + q) * 16 * RB + i * 1024), 16,
                                          0, kWeightPolicy);
       }
   };
@@ -874,20 +885,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
       const u32x4 fx = *(const u32x4*)(xs + xoff);
 #pragma unroll
       for (int q = 0; q < NS; ++q) {
-        const int coff = (wave * NS + q) * 2048 + r * 128 + ((j ^ ((r >> 1) & 7)) << 4) + 4 * g;
-        uint32_t w = *(const uint32_t*)(lc + coff);
+        // FP4: dword g of block j (8 codes); FP8: bytes 8 g .. 8 g + 7 of
+        // block j, which is chunks 2 j and 2 j + 1 of the row
+        const int base = (wave * NS + q) * 16 * RB + r * RB;
+        u32x2 w;
+        if (EB == 4) {
+          w[0] = *(const uint32_t*)(lc + base + ((j ^ ((r >> 1) & 7)) << 4) + 4 * g);
+          w[1] = 0u;
+        } else {
+          w = *(const u32x2*)(lc + base + (((2 * j + (g >> 1)) ^ r) << 4) + 8 * (g & 1));
+        }
         const int bj = min(8 * st + j, nb - 1);
         const uint32_t byte = lsc[q * SCS + srow + bj];
         asm volatile("" ::: "memory");  // keep reads of different arrays apart (a
                                         // merged read carries no alias information)
-        w = live ? w : 0u;
+        w[0] = live ? w[0] : 0u;
+        w[1] = live ? w[1] : 0u;
         const float scale =
             __uint_as_float(byte == 0 ? 0x00400000u : byte == 255 ? 0x7FC00000u : byte << 23);
         u32x4 fa;
-        fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-        fa[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-        fa[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-        fa[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+        if (EB == 4) {
+          fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 0));
+          fa[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 1));
+          fa[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 2));
+          fa[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 3));
+        } else {
+          fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], scale, false));
+          fa[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], scale, true));
+          fa[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], scale, false));
+          fa[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], scale, true));
+        }
         acc[q] = mfma16(fa, fx, acc[q]);
       }
     }
@@ -1073,9 +1100,12 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, block, 0, s, u);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP4 && P.up.bn == 16 * kMxUpWaves)
-    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMxUpWaves>), grid, dim3(64 * kMxUpWaves), 0, s,
+  if (P.kind == KIND_MXFP8)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMx8Waves, 8>), grid, dim3(64 * kMx8Waves), 0, s,
                        up_args(P, x));
+  else if (P.kind == KIND_MXFP4 && P.up.bn == 16 * kMxUpWaves)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMxUpWaves, 4>), grid, dim3(64 * kMxUpWaves), 0,
+                       s, up_args(P, x));
   else if (P.kind == KIND_MXFP4)
     hipLaunchKernelGGL(gemm_mx_stream_kernel<true>, grid, block, 0, s, up_args(P, x));
   else if (P.kind == KIND_BF16_DECODE)
@@ -1099,9 +1129,12 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, block, 0, s, dn);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP4 && P.down.bn == 16 * kMxDownWaves)
-    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMxDownWaves>), grid, dim3(64 * kMxDownWaves), 0,
-                       s, down_args(P, x));
+  if (P.kind == KIND_MXFP8)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMx8Waves, 8>), grid, dim3(64 * kMx8Waves), 0, s,
+                       down_args(P, x));
+  else if (P.kind == KIND_MXFP4 && P.down.bn == 16 * kMxDownWaves)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMxDownWaves, 4>), grid, dim3(64 * kMxDownWaves),
+                       0, s, down_args(P, x));
   else if (P.kind == KIND_MXFP4)
     hipLaunchKernelGGL(gemm_mx_stream_kernel<false>, grid, block, 0, s, down_args(P, x));
   else if (P.kind == KIND_BF16_DECODE)

@@ -19,7 +19,9 @@ static int prefill_rows(const moe_desc* d) {
 // reduction of at most kMxLdsMaxK use the LDS-staged kernel's wider tiles
 // (measured on the gpt-oss-shaped layer: faster from 32 tokens on, slower
 // at 1).
-static bool streaming(int kind) { return kind == KIND_BF16_DECODE || kind == KIND_MXFP4; }
+static bool streaming(int kind) {
+  return kind == KIND_BF16_DECODE || kind == KIND_MXFP4 || kind == KIND_MXFP8;
+}
 static bool mx_lds(const moe_desc* d, int K) {
   return (int64_t)d->T * d->k >= d->E && K <= kMxLdsMaxK;
 }
@@ -31,6 +33,7 @@ int up_row_tile(int kind, const moe_desc* d) {
 }
 int up_col_tile(int kind, const moe_desc* d) {
   if (kind == KIND_MXFP4) return mx_lds(d, d->d) ? 16 * kMxUpWaves : 32;
+  if (kind == KIND_MXFP8) return 16 * kMx8Waves;
   return kind == KIND_BF16_PREFILL ? 128 : streaming(kind) ? 16 : 32;
 }
 int down_row_tile(int kind, const moe_desc* d) {
@@ -38,6 +41,7 @@ int down_row_tile(int kind, const moe_desc* d) {
 }
 int down_col_tile(int kind, const moe_desc* d) {
   if (kind == KIND_MXFP4) return mx_lds(d, down_k(d)) ? 16 * kMxDownWaves : 32;
+  if (kind == KIND_MXFP8) return 16 * kMx8Waves;
   return kind == KIND_BF16_PREFILL ? 256 : streaming(kind) ? 16 : 32;
 }
 
@@ -58,9 +62,10 @@ static int validate(const moe_desc* d) {
     return MOE_ERR_INVALID_ARG;
   if (d->weighting != MOE_WEIGHTS_RENORM && d->weighting != MOE_WEIGHTS_RAW)
     return MOE_ERR_INVALID_ARG;
-  if (d->expert_format != MOE_EXPERTS_DENSE && d->expert_format != MOE_EXPERTS_MXFP4)
+  if (d->expert_format != MOE_EXPERTS_DENSE && d->expert_format != MOE_EXPERTS_MXFP4 &&
+      d->expert_format != MOE_EXPERTS_MXFP8)
     return MOE_ERR_INVALID_ARG;
-  if (d->expert_format == MOE_EXPERTS_MXFP4 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->expert_format != MOE_EXPERTS_DENSE && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->flags != 0) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d->capacity_factor) || d->capacity_factor < 0) return MOE_ERR_INVALID_ARG;
   const int64_t rows = d->T * (int64_t)(d->k + d->n_shared);
@@ -68,6 +73,9 @@ static int validate(const moe_desc* d) {
   const int q = d->dtype == MOE_BF16 ? 64 : 4;
   if (d->d % q || d->ffn % q) return MOE_ERR_UNSUPPORTED;
   if (d->n_shared > 0 && d->ffn_shared % q) return MOE_ERR_UNSUPPORTED;
+  if (d->expert_format == MOE_EXPERTS_MXFP8 &&
+      (d->d > kMx8MaxK || d->ffn > kMx8MaxK || (d->n_shared > 0 && d->ffn_shared > kMx8MaxK)))
+    return MOE_ERR_UNSUPPORTED;
   // The bf16 GEMMs address x, h and each expert's weight matrix with 32-bit
   // byte offsets.
   if (d->dtype == MOE_BF16) {
@@ -125,11 +133,13 @@ int make_plan(const moe_desc* d, Plan* p) {
     P.path = (T * d->k <= 8LL * d->E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   else
     P.path = d->path;
-  if (d->expert_format == MOE_EXPERTS_MXFP4) P.path = MOE_PATH_DECODE;
+  if (d->expert_format != MOE_EXPERTS_DENSE) P.path = MOE_PATH_DECODE;
   if (d->dtype == MOE_F32)
     P.kind = KIND_F32;
   else if (d->expert_format == MOE_EXPERTS_MXFP4)
     P.kind = KIND_MXFP4;
+  else if (d->expert_format == MOE_EXPERTS_MXFP8)
+    P.kind = KIND_MXFP8;
   else
     P.kind = P.path == MOE_PATH_DECODE ? KIND_BF16_DECODE : KIND_BF16_PREFILL;
 

@@ -31,6 +31,9 @@ constexpr int kRouteSigmoid = 1, kRouteRaw = 2;
 // kMxDownWaves for down); the direct-load kernel takes 16 x 32 tiles.
 constexpr int kMxLdsMaxK = 3072;
 constexpr int kMxUpWaves = 8, kMxDownWaves = 4;
+// MXFP8 experts: always the LDS-staged kernel, 4 waves (16 x 64 tiles), K
+// up to kMx8MaxK.
+constexpr int kMx8Waves = 4, kMx8MaxK = 8192;
 
 // One GEMM tile: rows [m0, m_end) of group g, output columns [n0, n0 + BN).
 // Entry 0 of a schedule is a header: {entries, row tiles, column tiles, 0}.
@@ -72,7 +75,13 @@ struct Plan {
       o_slot, o_idx, o_w, o_h, o_out, total;
 };
 
-enum KernelKind { KIND_F32 = 0, KIND_BF16_PREFILL = 1, KIND_BF16_DECODE = 2, KIND_MXFP4 = 3 };
+enum KernelKind {
+  KIND_F32 = 0,
+  KIND_BF16_PREFILL = 1,
+  KIND_BF16_DECODE = 2,
+  KIND_MXFP4 = 3,
+  KIND_MXFP8 = 4
+};
 
 // Fill `p` for `d`; returns a moe_status.
 int make_plan(const moe_desc* d, Plan* p);

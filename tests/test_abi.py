@@ -57,8 +57,14 @@ def test_desc_struct_size():
     (dict(capacity_factor=float("nan")), INVALID),
     (dict(capacity_factor=float("inf")), INVALID),
     (dict(expert_format=1), OK),
-    (dict(expert_format=2), INVALID),
+    (dict(expert_format=2), OK),
+    (dict(expert_format=3), INVALID),
     (dict(expert_format=1, dtype=0, d=64, ffn=64), INVALID),   # MXFP4 experts need bf16 x
+    (dict(expert_format=2, dtype=0, d=64, ffn=64), INVALID),   # so do MXFP8 experts
+    (dict(expert_format=2, d=8192, ffn=8192), OK),
+    (dict(expert_format=2, d=8256), UNSUPPORTED),              # MXFP8: K up to 8192
+    (dict(expert_format=2, ffn=8256), UNSUPPORTED),
+    (dict(expert_format=2, n_shared=1, ffn_shared=8256), UNSUPPORTED),
     (dict(T=2 ** 30, k=2), INVALID),
     (dict(d=96), UNSUPPORTED),
     (dict(ffn=100), UNSUPPORTED),
@@ -90,9 +96,11 @@ def test_workspace_and_paths():
     assert moe.moe_resolve_path(desc(T=4096, d=7168, E=256, k=8, ffn=2048, n_shared=1,
                                      ffn_shared=2048)) == "prefill"
     assert moe.moe_grouped_rows(desc(T=10, k=3, n_shared=2, ffn_shared=64)) == 50
-    # MXFP4 experts always run the streaming kernels
+    # MX-format experts always run the streaming kernels
     assert moe.moe_resolve_path(desc(T=4096, d=4096, E=8, k=2, ffn=14336,
                                      expert_format=1)) == "decode"
+    assert moe.moe_resolve_path(desc(T=4096, d=4096, E=8, k=2, ffn=8192,
+                                     expert_format=2)) == "decode"
 
 
 def test_entry_points_reject_before_launch():

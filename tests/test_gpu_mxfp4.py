@@ -43,14 +43,16 @@ SMALL = {c.name: c for c in [
 
 
 class MxCase:
-    def __init__(self, cfg, T=None, x=None):
+    def __init__(self, cfg, T=None, x=None, fmt="mxfp4"):
         self.cfg = cfg
+        self.fmt = fmt
         T = cfg.T if T is None else T
         self.w_router = generate.router_weight(cfg)
         self.bias = generate.normal_bias(cfg) if cfg.bias == "normal" else None
         self.x = x if x is not None else margin_x(cfg, T, self.w_router, self.bias)
-        self.mx = generate.stacked_mxfp4(cfg)
-        self.smx = generate.stacked_mxfp4(cfg, shared=True) if cfg.n_shared else None
+        stack = generate.stacked_mxfp4 if fmt == "mxfp4" else generate.stacked_mxfp8
+        self.mx = stack(cfg)
+        self.smx = stack(cfg, shared=True) if cfg.n_shared else None
 
     def expert(self, e):
         u, us, g, gs, d, ds = self.mx
@@ -65,7 +67,7 @@ class MxCase:
         c = self.cfg
         return oracle.moe_forward(self.x, self.w_router, self.bias, c.k, self.expert, c.E, "bf16",
                                   self.shared if c.n_shared else None, c.n_shared, tokens,
-                                  expert_dtype="mxfp4")
+                                  expert_dtype=self.fmt)
 
     def upload(self):
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -129,4 +131,53 @@ def test_mxfp4_gpt_oss_full_size(T):
     check_routing(idx, w, counts, ref)
     err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
     print(f"gpt_oss mxfp4 T={T}: max|err|/rms = {err:.3e}, touched {int((counts > 0).sum())}")
+    assert err <= TOL["bf16"], err
+
+
+# MXFP8 (E4M3 codes, one per byte): the LDS-staged kernel at every batch
+# size, 16 x 64 tiles with 4 waves; stage tails (K = 1280: 5 stages, 1024: 4),
+# partial tiles (ffn = 192), a shared expert, a single token, long K (4096).
+SMALL8 = {c.name: c for c in [
+    custom("mx8_ragged", 160, T=150, d=256, E=8, k=2, ffn=192),
+    custom("mx8_shared", 161, T=70, d=128, E=16, k=4, ffn=64, n_shared=1, ffn_shared=128,
+           bias="normal", bias_var=0.5),
+    custom("mx8_one_token", 162, T=1, d=192, E=8, k=2, ffn=128),
+    custom("mx8_stages", 163, T=64, d=1280, E=8, k=2, ffn=1024),
+    custom("mx8_long_k", 164, T=24, d=4096, E=4, k=2, ffn=128),
+]}
+
+
+@functools.lru_cache(maxsize=None)
+def case8_of(name):
+    return MxCase(SMALL8[name], fmt="mxfp8")
+
+
+@pytest.mark.parametrize("name", list(SMALL8))
+def test_mxfp8_small(name):
+    c = case8_of(name)
+    x, W = c.upload()
+    assert W.format == "mxfp8"
+    ref = c.oracle()
+    y, idx, w, counts = moe.moe_forward_mx(x, W, c.cfg.k, return_routing=True)
+    torch.cuda.synchronize()
+    check_routing(idx, w, counts, ref)
+    err = rel_err(y.cpu().numpy(), ref.y)
+    print(f"{name}: max|err|/rms = {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("T", [1, 128])
+def test_mxfp8_gpt_oss_full_size(T):
+    """The gpt-oss-shaped layer with MXFP8 experts: routing on every token,
+    y on samples."""
+    cfg = NAMED["gpt_oss"]
+    li = tables.layer_inputs(cfg, T)
+    c = MxCase(cfg, T, x=li.x, fmt="mxfp8")
+    x, W = c.upload()
+    ref = c.oracle(sample_tokens(T))
+    y, idx, w, counts = moe.moe_forward_mx(x, W, cfg.k, return_routing=True)
+    torch.cuda.synchronize()
+    check_routing(idx, w, counts, ref)
+    err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
+    print(f"gpt_oss mxfp8 T={T}: max|err|/rms = {err:.3e}")
     assert err <= TOL["bf16"], err

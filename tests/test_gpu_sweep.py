@@ -1,7 +1,7 @@
 """GPU parity on a seeded sweep of random layers: shapes, expert counts,
 top-k, shared experts, token counts (including a single token and counts
 just past a tile or token block), both expert paths, the router options and
-MXFP4 experts, each against the fp64 oracle on the same inputs.
+MXFP4 or MXFP8 experts, each against the fp64 oracle on the same inputs.
 
 The hand-picked cases elsewhere pin the known edge cases; this sweep draws
 combinations nobody chose, from a fixed seed so that a failure names a
@@ -135,10 +135,11 @@ MX_SWEEP = _draw_mx(16, 7)
                          ids=[f"{c.name}-T{c.T}-d{c.d}-E{c.E}k{c.k}-f{c.ffn}-sh{c.n_shared}"
                               for c in MX_SWEEP])
 def test_sweep_mxfp4(cfg):
-    """Random layers with MXFP4 experts (both MXFP4 kernels: the direct-load
-    one below one pair per expert, the LDS-staged one above)."""
+    """Random layers with MX-format experts: MXFP4 (even ids; both MXFP4
+    kernels: the direct-load one below one pair per expert, the LDS-staged
+    one above) and MXFP8 (odd ids)."""
     from test_gpu_mxfp4 import MxCase
-    c = MxCase(cfg)
+    c = MxCase(cfg, fmt="mxfp8" if cfg.config_id % 2 else "mxfp4")
     x, W = c.upload()
     ref = c.oracle()
     y, idx, w, counts = moe.moe_forward_mx(x, W, cfg.k, return_routing=True)
