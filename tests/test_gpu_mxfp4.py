@@ -115,7 +115,7 @@ def test_mxfp4_rejects_dense_entry_points():
                             None, None, None, None, 0, None, None) == -1
 
 
-@pytest.mark.parametrize("T", [1, 8, 32, 128])
+@pytest.mark.parametrize("T", [1, 8, 32, 128, 512])
 def test_mxfp4_gpt_oss_full_size(T):
     """The gpt-oss-shaped layer (d=2880, 128 experts, top-4) with MXFP4
     experts at decode batch sizes: routing on every token, y on samples
@@ -166,7 +166,7 @@ def test_mxfp8_small(name):
     assert err <= TOL["bf16"], err
 
 
-@pytest.mark.parametrize("T", [1, 128])
+@pytest.mark.parametrize("T", [1, 8, 32, 128, 512])
 def test_mxfp8_gpt_oss_full_size(T):
     """The gpt-oss-shaped layer with MXFP8 experts: routing on every token,
     y on samples."""
