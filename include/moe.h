@@ -108,7 +108,7 @@ typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } mo
 /* Routing weights: kept scores renormalised over the kept set, or raw. */
 typedef enum moe_weighting { MOE_WEIGHTS_RENORM = 0, MOE_WEIGHTS_RAW = 1 } moe_weighting;
 
-/* Storage of the expert weights: `dtype`, or MXFP4 (see the options above). */
+/* Storage of the expert weights: `dtype`, MXFP4 or MXFP8 (see the options above). */
 typedef enum moe_expert_format {
   MOE_EXPERTS_DENSE = 0,
   MOE_EXPERTS_MXFP4 = 1,
@@ -145,7 +145,7 @@ const char* moe_status_str(int status);
 /* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG (T<0, d/E/k/
  * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
  * n_shared > 0, bad enum, flags != 0, capacity_factor negative or not finite,
- * MXFP4 experts with dtype MOE_F32, T*(k+n_shared) >= 2^31) or
+ * MXFP4 or MXFP8 experts with dtype MOE_F32, T*(k+n_shared) >= 2^31) or
  * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
  * 64, or with x (T*d), h ((T*(k+n_shared)+256)*max ffn) or one expert's
  * weight matrix (max ffn * d) reaching 4 GiB, as the bf16 kernels address
@@ -181,7 +181,8 @@ int64_t moe_grouped_rows(const moe_desc* desc);
  *   workspace    >= moe_workspace_size(desc) bytes, 256-byte aligned
  * x, w_router and the expert weight arrays are 16-byte aligned (the kernels
  * read them in 16-byte chunks; MOE_ERR_INVALID_ARG otherwise).
- * A layer with MXFP4 experts needs moe_forward_mx (MOE_ERR_INVALID_ARG here).
+ * A layer with MXFP4 or MXFP8 experts needs moe_forward_mx (MOE_ERR_INVALID_ARG
+ * here).
  */
 int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 const float* router_bias, const void* w_up, const void* w_gate,
@@ -190,7 +191,7 @@ int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                 moe_stream stream);
 
-/* Scale arrays of MXFP4 expert weights (uint8 E8M0, one per 32 elements
+/* Scale arrays of MXFP4 or MXFP8 expert weights (uint8 E8M0, one per 32 elements
  * along K): up, gate [E,ffn,d/32], down [E,d,ffn/32]; shared-expert
  * counterparts [n_shared,...] or NULL when n_shared == 0. */
 typedef struct moe_mx_scales {
@@ -207,7 +208,8 @@ typedef struct moe_mx_scales {
  * [E,ffn,d/2], w_down [E,d,ffn/2] (and the shared counterparts) hold the
  * packed E2M1 codes, `scales` their E8M0 scales (16-byte aligned like the
  * codes).  With MOE_EXPERTS_MXFP8 the code arrays hold one E4M3 byte per
- * element: w_up, w_gate [E,ffn,d], w_down [E,d,ffn].  Every other argument is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
+ * element: w_up, w_gate [E,ffn,d], w_down [E,d,ffn].  Every other argument
+ * is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
  * moe_forward_timed.  Scale bytes 0 (2^-127) and 255 (NaN) follow the format
  * but results that leave bfloat16's normal range are not defined.
  */
@@ -270,7 +272,7 @@ int moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* expert_
  * down).  For grouped row r of group g with token t = sorted_token[r]:
  *   expert_out[r,:] = FFN_g(x[t,:])       float32 [T*(k+n_shared), d]
  * group_offsets / sorted_token as produced by moe_dispatch.  Dense expert
- * weights only (MOE_ERR_INVALID_ARG for MXFP4).  x and the weight arrays are
+ * weights only (MOE_ERR_INVALID_ARG for MXFP4 or MXFP8).  x and the weight arrays are
  * 16-byte aligned (MOE_ERR_INVALID_ARG otherwise).
  */
 int moe_experts(const moe_desc* desc, const void* x, const void* w_up, const void* w_gate,

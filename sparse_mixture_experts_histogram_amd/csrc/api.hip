@@ -57,7 +57,7 @@ namespace {
 // moe_forward's launch sequence; events[i] (when non-null) is recorded on the
 // stream before launch i (router, dispatch, up/gate, down, combine) and
 // events[5] after the last one.
-// `mx` is the scale set of MXFP4 expert weights (null for dense weights).
+// `mx` is the scale set of MXFP4 or MXFP8 expert weights (null for dense weights).
 int forward_impl(const moe_desc* d, const void* x, const void* w_router,
                  const float* router_bias, const void* w_up, const void* w_gate,
                  const void* w_down, const void* ws_up, const void* ws_gate, const void* ws_down,

@@ -47,8 +47,8 @@ struct GemmArgs {
   int ksplit;                 // K ranges per tile (partial sums to separate outputs)
   int64_t split_stride;       // elements between the outputs of consecutive K ranges
   uint32_t tok_bytes;         // bytes of tok (the buffer range of its DMA)
-  // MXFP4 experts: w0/w1/s0/s1 hold E2M1 codes [., N, K/2] and these their
-  // E8M0 scales [., N, K/32]
+  // MX-format experts: w0/w1/s0/s1 hold E2M1 codes [., N, K/2] (MXFP4) or
+  // E4M3 codes [., N, K] (MXFP8) and these their E8M0 scales [., N, K/32]
   const uint8_t *sw0, *sw1, *ss0, *ss1;
 };
 
@@ -743,10 +743,11 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
   }
 }
 
-// MXFP4 weights through LDS, for batches with about one (token, expert) pair
-// per expert and more: a tile is 16 rows x 16 NW features, one wave per 16
-// features over the whole of K, so the token slab in LDS is shared by NW
-// waves (the direct-load kernel above re-reads it per wave).  K streams in
+// MXFP4 (EB = 4) or MXFP8 (EB = 8) weights through LDS, for batches with
+// about one (token, expert) pair per expert and more: a tile is 16 rows x
+// 16 NW features, one wave per 16 features over the whole of K, so the
+// token slab in LDS is shared by NW waves (the direct-load kernel above
+// re-reads it per wave).  K streams in
 // stages of 256 (eight 32-k blocks) through a 3-stage ring of LDS copies: a
 // stage holds the 16 x 256 token slab (8 KB, every wave copies 8 KB / NW
 // of it) and, per wave and weight matrix, 16 feature rows x 128 code bytes

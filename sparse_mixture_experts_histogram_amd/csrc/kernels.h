@@ -38,7 +38,7 @@ hipError_t launch_dispatch(const Plan& P, const int32_t* idx, int32_t* blk_hist,
 hipError_t launch_tiles(const Plan& P, const int32_t* offsets, Tile* tiles_up, Tile* tiles_down,
                         hipStream_t s);
 
-// E8M0 scale arrays of MXFP4 expert weights (all null for dense weights).
+// E8M0 scale arrays of MXFP4 or MXFP8 expert weights (all null for dense weights).
 struct MxScales {
   const uint8_t *up, *gate, *down, *s_up, *s_gate, *s_down;
 };
@@ -53,7 +53,7 @@ struct ExpertArgs {
   float* out;     // expert outputs; with ksplit > 1, ksplit partial buffers of
                   // (R + kRowSlack) rows each, summed by the combine
   int ksplit;     // K ranges of the down GEMM (1 = direct result)
-  MxScales mx;    // MXFP4 expert weights: their scales
+  MxScales mx;    // MX-format expert weights: their scales
 };
 
 // Grouped up/gate GEMM + SwiGLU (writes h).
