@@ -1,7 +1,7 @@
 """GPU parity on a seeded sweep of random layers: shapes, expert counts,
 top-k, shared experts, token counts (including a single token and counts
 just past a tile or token block), both expert paths, the router options and
-MXFP4 or MXFP8 experts, each against the fp64 oracle on the same inputs.
+MXFP4 or MXFP8 experts (also with reductions up to 3072), each against the fp64 oracle on the same inputs.
 
 The hand-picked cases elsewhere pin the known edge cases; this sweep draws
 combinations nobody chose, from a fixed seed so that a failure names a
@@ -185,3 +185,43 @@ def test_sweep_medium(item):
     err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
     print(f"{_id(item)}: max|err|/rms = {err:.3e}")
     assert err <= TOL[cfg.dtype], err
+
+
+def _draw_mx_medium(n: int, seed: int):
+    """MX-format layers with long reductions (d and ffn up to 3072: several
+    LDS stages, many column tiles) and both batch regimes (fewer pairs than
+    experts, and more); even ids MXFP4, odd ids MXFP8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        E = int(rng.choice([8, 32, 128]))
+        d = 64 * int(rng.integers(16, 49))
+        ffn = 64 * int(rng.integers(8, 49))
+        if E * d * ffn > 1 << 27:
+            continue
+        k = int(rng.integers(1, 5))
+        n_sh = int(rng.choice([0, 1]))
+        out.append(custom(f"mxmed{i}", 600 + i, T=int(rng.choice([1, 5, 64, 300])), d=d, E=E,
+                          k=k, ffn=ffn, n_shared=n_sh, ffn_shared=64 * int(rng.integers(8, 33)) if n_sh else 0,
+                          bias="normal" if rng.random() < 0.3 else "none", bias_var=0.5))
+    return out
+
+
+MX_MED_SWEEP = _draw_mx_medium(6, 13)
+
+
+@pytest.mark.parametrize("cfg", MX_MED_SWEEP,
+                         ids=[f"{c.name}-T{c.T}-d{c.d}-E{c.E}k{c.k}-f{c.ffn}-sh{c.n_shared}"
+                              for c in MX_MED_SWEEP])
+def test_sweep_mx_medium(cfg):
+    from test_gpu_mxfp4 import MxCase
+    c = MxCase(cfg, fmt="mxfp8" if cfg.config_id % 2 else "mxfp4")
+    x, W = c.upload()
+    ref = c.oracle(sample_tokens(cfg.T))
+    y, idx, w, counts = moe.moe_forward_mx(x, W, cfg.k, return_routing=True)
+    torch.cuda.synchronize()
+    check_routing(idx, w, counts, ref)
+    err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
+    print(f"{cfg.name} ({c.fmt}): max|err|/rms = {err:.3e}")
+    assert err <= TOL["bf16"], err
