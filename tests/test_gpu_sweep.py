@@ -225,3 +225,39 @@ def test_sweep_mx_medium(cfg):
     err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
     print(f"{cfg.name} ({c.fmt}): max|err|/rms = {err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+def _draw_f32_medium(n: int, seed: int):
+    """fp32 layers beyond the small sweep's sizes: d and ffn up to 1024, up to
+    1500 tokens (many tiles of the fp32 GEMM), held to the fp32 bar."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([4, 8, 16, 64]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        n_sh = int(rng.choice([0, 1]))
+        cfg = custom(f"f32med{i}", 700 + i, T=int(rng.integers(200, 1500)),
+                     d=4 * int(rng.integers(32, 257)), E=E, k=k,
+                     ffn=4 * int(rng.integers(32, 257)), n_shared=n_sh,
+                     ffn_shared=4 * int(rng.integers(16, 129)) if n_sh else 0, dtype="f32",
+                     bias="normal" if rng.random() < 0.4 else "none", bias_var=0.5)
+        out.append((cfg, Options(scoring="sigmoid" if rng.random() < 0.3 else "softmax"), "auto"))
+    return out
+
+
+F32_MED_SWEEP = _draw_f32_medium(4, 17)
+
+
+@pytest.mark.parametrize("item", F32_MED_SWEEP, ids=[_id(s) for s in F32_MED_SWEEP])
+def test_sweep_f32_medium(item):
+    cfg, opts, path = item
+    c = make_case(cfg, opts=opts)
+    x, W = upload(c)
+    ref = c.oracle(sample_tokens(cfg.T))
+    y, idx, w, counts = moe.moe_forward(x, W, cfg.k, path=path, return_routing=True,
+                                        routing=moe.Routing(scoring=opts.scoring))
+    torch.cuda.synchronize()
+    check_routing(idx, w, counts, ref)
+    err = rel_err(y.cpu().numpy()[ref.tokens], ref.y)
+    print(f"{_id(item)}: max|err|/rms = {err:.3e}")
+    assert err <= TOL["f32"], err
