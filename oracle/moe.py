@@ -235,7 +235,8 @@ def route(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: in
 
 def expert_capacity(T: int, k: int, E: int, factor: float) -> int:
     """Most (token, slot) pairs one expert takes: ceil(T*k/E * factor),
-    evaluated in that order in IEEE double (P4's capacity line)."""
+    evaluated in that order in IEEE double (page "Mixture of Experts Explained: Routers, Active Parameters and VRAM",
+    "Noise and the second expert": its capacity formula)."""
     return math.ceil(T * k / E * factor)
 
 
@@ -278,9 +279,11 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 def swiglu_expert(X: np.ndarray, w_up: np.ndarray, w_gate: np.ndarray,
                   w_down: np.ndarray) -> np.ndarray:
-    """One gated expert FFN (P4: a gated block with three matrices; P2 "Where
-    MoE changes the Transformer": two linear layers with an activation between
-    them): SiLU(X W_gate^T) * (X W_up^T), then times W_down^T.
+    """One gated expert FFN (page "Mixture of Experts Explained: Routers, Active Parameters and VRAM",
+    the active-parameter arithmetic: a gated block with three matrices; page
+    "Mixture of Experts: why a model with 671 billion parameters uses only
+    37", "Where MoE changes the Transformer": two linear layers with an
+    activation between them): SiLU(X W_gate^T) * (X W_up^T), then times W_down^T.
     X [n,d]; w_up, w_gate [f,d]; w_down [d,f] -> [n,d]."""
     U = X @ w_up.T
     G = X @ w_gate.T

@@ -95,8 +95,9 @@ def torch_ffn(xrow, wu, wg, wd):
 
 
 def brute_force_y(x, wr, b, ex, sh, k):
-    """Dense evaluation (P4: the loop matched a slow version that runs every
-    expert with zero weight for the unpicked ones): every token through every
+    """Dense evaluation (page "Mixture of Experts Explained: Routers, Active Parameters and VRAM",
+    "Why MoE models can feel fast anyway": the loop matched a slow version
+    that runs every expert with zero weight for the unpicked ones): every token through every
     expert, gated by a length-E vector that is zero off the top-k.  The top-k
     set is the k-subset with the largest logit sum, over all subsets; the
     weights are library softmax probabilities renormalised over that set."""
@@ -233,8 +234,9 @@ def check_occupancy_table():
 
 def check_occupancy_monte_carlo(trials=3000, seed=7):
     """Routing with iid logits is uniform over k-subsets, so the mean touched
-    share matches the closed form (P3: a Monte Carlo run agreed within 0.05
-    percentage points)."""
+    share matches the closed form (page "Mixture of experts: how MoE works
+    and what it costs", "How batching changes the mixture of experts math": a
+    Monte Carlo run agreed within 0.05 percentage points)."""
     rng = np.random.default_rng(seed)
     for k, E, B in ((2, 8, 4), (8, 256, 16), (4, 128, 8)):
         shares = np.empty(trials)
@@ -316,7 +318,8 @@ def check_raw_softmax_weights(seed=22, T=80, d=12, E=6):
 
 
 def check_capacity_closed_forms():
-    """P4's capacity line: ceil(tokens * k / experts * factor).  On the page's
+    """The capacity formula of page "Mixture of Experts Explained: Routers, Active Parameters and VRAM",
+    "Noise and the second expert": ceil(tokens * k / experts * factor).  On the page's
     printed tokens-per-expert list (512 tokens, top-2, 8 experts) factor 1.0
     gives 128 and drops (135-128)+(147-128)+(133-128) = 31 slots; factors 1.25
     and 2.0 drop none (the page: an even router drops nothing at 1.25)."""
