@@ -32,11 +32,16 @@ from moe_inputs.configs import MoEConfig
 from . import moe
 
 
+def zipf_target(E: int, s: float) -> np.ndarray:
+    """Zipf(s) load shares over ranks r = 1..E: r^-s / sum_q q^-s."""
+    r = np.arange(1, E + 1, dtype=np.float64)
+    target = r ** (-s)
+    return target / target.sum()
+
+
 def calibrate_zipf(cfg: MoEConfig, x_raw: np.ndarray, w_r: np.ndarray, rounds: int = 60):
     E, k = cfg.E, cfg.k
-    r = np.arange(1, E + 1, dtype=np.float64)
-    target = r ** (-cfg.zipf_s)
-    target /= target.sum()
+    target = zipf_target(E, cfg.zipf_s)
     L0 = moe.router_logits(moe.widen(x_raw, cfg.dtype), moe.widen(w_r, cfg.dtype), None)
     b = np.log(target)
     for _ in range(rounds):

@@ -543,6 +543,118 @@ def check_mxfp8_layer_bruteforce(seed=30, T=10, d=64, E=3, k=2, f=32):
     assert np.max(np.abs(r.y - y)) / np.sqrt(np.mean(y ** 2)) < 1e-12
 
 
+# ---------------------------------------------------------------- routing margin
+def _gap_pairs(row, k):
+    """Smallest |L_a - L_b| over pairs whose first member is one of the k kept
+    experts (found as the k-subset with the largest sum, over all subsets) and
+    whose second is any other expert.  Pairs with both members outside the
+    kept set do not bound how far the kept list can move."""
+    E = len(row)
+    if E < 2:
+        return math.inf
+    best = max(itertools.combinations(range(E), k), key=lambda c: sum(row[list(c)]))
+    return min(abs(row[a] - row[b]) for a in best for b in range(E) if b != a)
+
+
+def _ordered_topk(row, k):
+    """The kept experts in descending score order, ties to the lower index,
+    by Python's sort on (-score, index)."""
+    return sorted(range(len(row)), key=lambda e: (-row[e], e))[:k]
+
+
+def check_topk_gaps_hand_rows():
+    """Rows with a known smallest gap, placed inside the kept list, between the
+    last kept and the first dropped expert, or only among dropped experts
+    (which must not count), each in shuffled column order; k = E; E = 1."""
+    rows = [  # (row, k, gap)
+        ([3.0, 2.9999, 1.0, 0.0], 2, 1e-4),          # inside the kept list
+        ([3.0, 2.0, 1.9999, 0.0], 2, 1e-4),          # between ranks k and k+1
+        ([3.0, 2.0, 1.0, 0.9999], 2, 1.0),           # only between dropped ranks
+        ([3.0, 2.0, 1.0, 0.5, 0.49999], 3, 0.5),     # ranks k+1 and k+2 do not count
+        ([5.0, 4.0, 3.5, -1.0, -1.0], 3, 0.5),       # exact tie among dropped experts
+        ([0.25, 1.5, 1.0], 3, 0.5),                  # k = E: every consecutive gap
+        ([0.25, 1.5, 1.0], 2, 0.5),                  # E = k + 1
+        ([2.0, 2.0, 1.0], 1, 0.0),                   # tie at the top
+        ([7.0, -3.0], 1, 10.0),
+    ]
+    rng = np.random.default_rng(31)
+    for row, k, gap in rows:
+        for _ in range(4):
+            perm = rng.permutation(len(row))
+            got = om.topk_gaps(np.array(row)[perm][None, :], k)[0]
+            assert abs(got - gap) < 1e-12, (row, k, gap, got)
+    assert om.topk_gaps(np.array([[1.3]]), 1)[0] == math.inf
+
+
+def check_topk_gaps_pairs(seed=32):
+    """Against the pair brute force on random rows (some with repeated values),
+    for every k from 1 to E."""
+    rng = np.random.default_rng(seed)
+    for E in (2, 3, 5, 8):
+        L = np.round(rng.standard_normal((60, E)) * 3, 1)  # coarse grid: ties happen
+        for k in range(1, E + 1):
+            got = om.topk_gaps(L, k)
+            want = np.array([_gap_pairs(L[t], k) for t in range(L.shape[0])])
+            assert np.allclose(got, want, rtol=0, atol=1e-12), (E, k)
+
+
+def check_topk_gaps_meaning(seed=33):
+    """What the margin promises: a row whose gap is g keeps the same ordered
+    top k under any perturbation smaller than g/2 in every entry, and a
+    perturbation of g/2 (plus a little) aimed at the pair that realises the
+    gap changes it."""
+    rng = np.random.default_rng(seed)
+    for E, k in ((6, 2), (8, 3), (4, 4), (5, 1)):
+        L = rng.standard_normal((40, E))
+        g = om.topk_gaps(L, k)
+        for t in range(L.shape[0]):
+            base = _ordered_topk(L[t], k)
+            for _ in range(20):
+                d = rng.uniform(-1, 1, E) * g[t] / 2 * (1 - 1e-9)
+                assert _ordered_topk(L[t] + d, k) == base, (E, k, t)
+            # the realising pair: a kept expert a and any other b at distance g
+            pairs = [(a, b) for a in base for b in range(E)
+                     if b != a and abs(L[t, a] - L[t, b]) <= g[t] * (1 + 1e-12)]
+            assert pairs, (E, k, t)
+            a, b = pairs[0]
+            hi, lo = (a, b) if L[t, a] > L[t, b] else (b, a)
+            d = np.zeros(E)
+            step = g[t] / 2 * (1 + 1e-6) + 1e-12
+            d[hi] -= step
+            d[lo] += step
+            assert _ordered_topk(L[t] + d, k) != base, (E, k, t)
+
+
+# ---------------------------------------------------------------- Zipf target
+def zipf_shares(E, s):
+    """Zipf(s) over ranks 1..E: p_r = r^-s / sum_q q^-s, summed term by term."""
+    w = [1.0 / r ** s for r in range(1, E + 1)]
+    tot = math.fsum(w)
+    return [v / tot for v in w]
+
+
+def check_zipf_targets(E=32, s=1.1):
+    """The mid-size layer's target load shares are Zipf(1.1) over the 32
+    experts, expert r-1 at rank r: both the stored table (6 decimals) and the
+    table script's target function."""
+    from oracle import make_input_tables as mit
+    want = zipf_shares(E, s)
+    for target, atol in ((golden_table("midsize_zipf")["target_shares"], 5e-7),
+                         (list(mit.zipf_target(E, s)), 1e-15)):
+        assert len(target) == E
+        assert max(abs(a - b) for a, b in zip(target, want)) <= atol, (target[:3], want[:3])
+    assert len(target) == E
+    assert max(abs(a - b) for a, b in zip(target, want)) <= atol, (target[:3], want[:3])
+    # spot values: the hottest expert takes 28.4%, the coldest 0.63%
+    assert round(100 * want[0], 1) == 28.4 and round(100 * want[-1], 2) == 0.63
+
+
+def golden_table(name):
+    tab = os.path.join(os.path.dirname(GOLDEN), os.pardir, "moe_inputs", "tables", name + ".json")
+    with open(tab) as f:
+        return json.load(f)
+
+
 ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, check_tie_break,
        check_softmax_library, check_invariants, check_uniform_gates,
        check_single_expert_library, check_silu, check_widen, check_occupancy_table,
@@ -551,4 +663,5 @@ ALL = [check_worked_example_routing, check_brute_force, check_topk_bruteforce, c
        check_capacity_bruteforce, check_sigmoid_layer_bruteforce, check_e2m1_table,
        check_e8m0_library, check_mxfp4_dequant, check_mxfp4_layer_bruteforce,
        check_e4m3_library, check_e4m3_closed_forms, check_mxfp8_dequant,
-       check_mxfp8_layer_bruteforce]
+       check_mxfp8_layer_bruteforce, check_topk_gaps_hand_rows, check_topk_gaps_pairs,
+       check_topk_gaps_meaning, check_zipf_targets]

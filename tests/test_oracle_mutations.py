@@ -130,7 +130,62 @@ def _dequant8_block16(codes, scales):
     sc = 2.0 ** (np.asarray(scales, np.int64)[:, (np.arange(K) // 16) % nb] - 127)
     return table[codes] * sc
 
+def _gaps_last_only(L, k):
+    s = -np.sort(-L, axis=-1)[:, :min(k + 1, L.shape[1])]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return s[:, -2] - s[:, -1]
+
+
+def _gaps_k_values(L, k):
+    s = -np.sort(-L, axis=-1)[:, :k]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return np.min(s[:, :-1] - s[:, 1:], axis=-1)
+
+
+def _gaps_k_plus_2(L, k):
+    s = -np.sort(-L, axis=-1)[:, :k + 2]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return np.min(s[:, :-1] - s[:, 1:], axis=-1)
+
+
+def _gaps_ascending(L, k):
+    s = np.sort(L, axis=-1)[:, :min(k + 1, L.shape[1])]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return np.min(np.abs(s[:, :-1] - s[:, 1:]), axis=-1)
+
+
+def _gaps_unsorted(L, k):
+    s = L[:, :min(k + 1, L.shape[1])]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return np.min(np.abs(s[:, :-1] - s[:, 1:]), axis=-1)
+
+
+def _zipf_wrong_exponent(E, s):
+    r = np.arange(1, E + 1, dtype=np.float64)
+    t = r ** (-1.0)
+    return t / t.sum()
+
+
+def _zipf_from_zero(E, s):
+    r = np.arange(0, E, dtype=np.float64) + 2.0
+    t = r ** (-s)
+    return t / t.sum()
+
+
 MUTANTS = [
+    ("topk_gaps", _gaps_last_only, P.check_topk_gaps_hand_rows),
+    ("topk_gaps", _gaps_last_only, P.check_topk_gaps_pairs),
+    ("topk_gaps", _gaps_k_values, P.check_topk_gaps_hand_rows),
+    ("topk_gaps", _gaps_k_values, P.check_topk_gaps_meaning),
+    ("topk_gaps", _gaps_k_plus_2, P.check_topk_gaps_hand_rows),
+    ("topk_gaps", _gaps_k_plus_2, P.check_topk_gaps_pairs),
+    ("topk_gaps", _gaps_ascending, P.check_topk_gaps_hand_rows),
+    ("topk_gaps", _gaps_unsorted, P.check_topk_gaps_pairs),
     ("e2m1_value", _e2m1_bias2, P.check_e2m1_table),
     ("e8m0_value", _e8m0_bias128, P.check_e8m0_library),
     ("dequant_mxfp4", _dequant_high_nibble_first, P.check_mxfp4_dequant),
@@ -168,6 +223,17 @@ def test_mutant_is_caught(monkeypatch, name, bad, check):
     monkeypatch.setattr(om, name, bad)
     with pytest.raises(AssertionError):
         check()
+
+
+ZIPF_MUTANTS = [_zipf_wrong_exponent, _zipf_from_zero]
+
+
+@pytest.mark.parametrize("bad", ZIPF_MUTANTS, ids=lambda f: f.__name__)
+def test_zipf_mutant_is_caught(monkeypatch, bad):
+    from oracle import make_input_tables as mit
+    monkeypatch.setattr(mit, "zipf_target", bad)
+    with pytest.raises(AssertionError):
+        P.check_zipf_targets()
 
 
 def test_dropped_shared_expert_is_caught(monkeypatch):
