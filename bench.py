@@ -1,13 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Workload: the Mixtral-shaped layer (d=4096, E=8, top-2, SwiGLU ffn=14336, bf16
-storage, fp32 accumulation) at T=4096 tokens (prefill).  One step is one
-moe_forward over the whole batch (router, dispatch, both grouped GEMMs,
-combine), inputs and weights already resident in HBM.  The same layer at T=16
-(decode) is timed too and reported under "decode".
+Headline workload: the Mixtral-shaped layer (d=4096, E=8, top-2, SwiGLU
+ffn=14336, bf16 storage, fp32 accumulation) at T=4096 tokens (prefill).  One
+step is one moe_forward over the whole batch (router, dispatch, both grouped
+GEMMs, combine), inputs and weights already resident in HBM.
+
+The same run times every other named layer and reports each under
+"configs" with tokens/s and its roofline fraction: the Mixtral-shaped layer
+at T=16 (decode), the mid-size Zipf layer at T=8192, the DeepSeek-V3-shaped
+layer at T=4096 and the gpt-oss-shaped layer at T = 1, 8, 32, 128, 512.
+Token rows, router weights and biases are the seeded, margin-filtered inputs
+the parity tests use (they steer the routing); the expert weights of those
+layers are filled on the device with seeded N(0, 1/fan_in) values, since
+their values do not steer any kernel.
 
 Prints ONE JSON line with the metric, the live roofline figure of the
 dominant kernel (the up/gate grouped GEMM, timed with hipEvents recorded on
@@ -31,6 +39,20 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM % MFMA peak (prefill), % HBM peak (
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
+# name -> (named layer, T, timing): "steps" = mean over back-to-back steps,
+# "flushed" = median over iterations with L2 and MALL flushed in between
+WORKLOADS = {
+    "mixtral_t4096": ("mixtral", 4096, "steps"),
+    "mixtral_t16": ("mixtral", 16, "flushed"),
+    "midsize_zipf_t8192": ("midsize_zipf", 8192, "steps"),
+    "deepseek_v3_t4096": ("deepseek_v3", 4096, "steps"),
+    "gpt_oss_t1": ("gpt_oss", 1, "flushed"),
+    "gpt_oss_t8": ("gpt_oss", 8, "flushed"),
+    "gpt_oss_t32": ("gpt_oss", 32, "flushed"),
+    "gpt_oss_t128": ("gpt_oss", 128, "flushed"),
+    "gpt_oss_t512": ("gpt_oss", 512, "flushed"),
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -48,6 +70,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle runs (median taken)")
+    ap.add_argument("--workload", default="all",
+                    help="'all' (default: the headline plus every config), or one of "
+                         + ", ".join(WORKLOADS) + " to time that layer alone (for profiling)")
     ap.add_argument("--variants", action="store_true",
                     help="also time the router options: sigmoid / raw routing on the "
                          "DeepSeek-V3-shaped router, capacity cuts on the Mixtral-shaped "
@@ -163,13 +188,17 @@ def decode_leg(cfg, x, W, k, iters):
     dec_layer, dec_gemm, dec_counts = time_decode(xd, W, k, iters)
     touched = int(np.sum(dec_counts > 0))
     touched_bytes = touched * 3 * cfg.d * cfg.ffn * 2
+    fig = layer_figures(cfg, 16, dec_layer, dec_counts)
+    fig["expert_gemms_ms"] = round(dec_gemm, 4)
+    fig["grouped_gemm_hbm_frac"] = round(touched_bytes / (dec_gemm * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)
+    fig["timing"] = (f"median of {iters} hipEvent-timed layers, L2 and MALL flushed between them")
     dec = {"T": 16, "ms_per_step": round(dec_layer, 4), "tokens_per_s": round(16 / dec_layer * 1e3, 1),
            "experts_touched": touched, "touched_weight_bytes": touched_bytes,
            "hbm_frac_layer": round(touched_bytes / (dec_layer * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
            "hbm_frac_expert_gemms": round(touched_bytes / (dec_gemm * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
            "timing": "median of per-iteration hipEvent times (events before the first and after the "
-                     "last launch only), L2 and MALL flushed by a 1 GiB read between iterations"}
-
+                     "last launch only), L2 and MALL flushed by a 1 GiB read between iterations",
+           "figures": fig}
     return dec
 
 
@@ -336,24 +365,148 @@ def cpu_baseline(cfg, li, sample, reps):
         oracle.moe_forward(xs, li.w_router, li.bias, cfg.k, lambda e: wts[e], cfg.E, cfg.dtype)
         times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
+    info = host_info()
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": info["cpu"], "blas": info["blas"],
             "sample": f"first {sample} tokens of the {cfg.name} T={cfg.T} workload (routing + "
                       f"chosen experts), fp64 numpy oracle, median of {reps} runs of "
                       f"{dt:.2f} s each ({sum(times):.1f} s total)"}
+
+
+def upload_routing_inputs(cfg, T, seed=1234):
+    """Seeded, margin-filtered token rows, router weight and bias of a named
+    layer (what steers the routing), and expert weights filled on the device
+    with N(0, 1/fan_in) values from a seeded torch generator."""
+    import numpy as np
+    import torch
+    import sparse_mixture_experts_histogram_amd as moe
+    from moe_inputs import tables
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    li = tables.layer_inputs(cfg, T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + cfg.config_id)
+
+    def fill(n, rows, cols):
+        out = torch.empty((n, rows, cols), dtype=torch.bfloat16, device="cuda")
+        for e in range(n):  # one matrix at a time: no large float32 temporary
+            out[e].copy_(torch.randn((rows, cols), generator=g, device="cuda")
+                         .mul_(1.0 / cols ** 0.5))
+        return out
+
+    W = moe.Weights(w_router=dev(li.w_router), w_up=fill(cfg.E, cfg.ffn, cfg.d),
+                    w_gate=fill(cfg.E, cfg.ffn, cfg.d), w_down=fill(cfg.E, cfg.d, cfg.ffn),
+                    bias=None if li.bias is None else torch.from_numpy(li.bias).cuda())
+    if cfg.n_shared:
+        W.ws_up = fill(cfg.n_shared, cfg.ffn_shared, cfg.d)
+        W.ws_gate = fill(cfg.n_shared, cfg.ffn_shared, cfg.d)
+        W.ws_down = fill(cfg.n_shared, cfg.d, cfg.ffn_shared)
+    return li, dev(li.x), W
+
+
+def layer_figures(cfg, T, ms, counts, per=None):
+    """tokens/s and roofline fractions of one layer time.  Algorithmic FLOPs:
+    2*T*d*E for the router plus 2 per weight per (token, expert) pair (the
+    shared experts included).  Bytes: the touched experts' weights (an expert
+    with at least one pair, and every shared expert), the router matrix, x,
+    y in fp32 and the routing indices and weights; padding and the
+    intermediates h and expert outputs are implementation traffic and are not
+    counted."""
+    import numpy as np
+    eb = cfg.elem_bytes
+    touched = int(np.sum(np.asarray(counts) > 0))
+    w_bytes = (touched * 3 * cfg.d * cfg.ffn + cfg.n_shared * 3 * cfg.d * cfg.ffn_shared) * eb
+    alg_bytes = (w_bytes + cfg.E * cfg.d * eb + T * cfg.d * eb + T * cfg.d * 4 + T * cfg.k * 8)
+    flops = cfg.flops(T)
+    out = {"T": T, "ms": round(ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
+           "experts_touched": touched, "touched_weight_bytes": w_bytes,
+           "algorithmic_bytes": alg_bytes, "algorithmic_flops": flops,
+           "hbm_frac_touched_weights": round(w_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+           "hbm_frac_algorithmic": round(alg_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+           "mfma_frac": round(flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)}
+    if per is not None:
+        out["kernels_ms"] = {n: round(v, 4) for n, v in per.items()}
+        pairs = T * cfg.k
+        f_up = 4.0 * cfg.d * (cfg.ffn * pairs + cfg.ffn_shared * T * cfg.n_shared)
+        out["grouped_gemm_mfma_frac"] = round(
+            1.5 * f_up / ((per["expert_up"] + per["expert_down"]) * 1e-3)
+            / (PEAK_BF16_TFLOPS * 1e12), 4)
+        out["grouped_gemm_hbm_frac"] = round(
+            w_bytes / ((per["expert_up"] + per["expert_down"]) * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)
+    return out
+
+
+def run_workload(name, steps, warmup, iters):
+    """Time one named workload on device-filled expert weights."""
+    import torch
+    from moe_inputs import NAMED
+    layer, T, how = WORKLOADS[name]
+    cfg = NAMED[layer]
+    t0 = time.perf_counter()
+    li, x, W = upload_routing_inputs(cfg, T)
+    torch.cuda.synchronize()
+    t_in = time.perf_counter() - t0
+    if how == "steps":
+        wall, _, per, counts = time_forward(x, W, cfg.k, steps, warmup)
+        fig = layer_figures(cfg, T, wall * 1e3, counts, per)
+        fig["timing"] = f"mean of {steps} back-to-back steps (wall clock), per-kernel hipEvents"
+    else:
+        ms, gemm, counts = time_decode(x, W, cfg.k, iters)
+        fig = layer_figures(cfg, T, ms, counts)
+        fig["expert_gemms_ms"] = round(gemm, 4)
+        fig["grouped_gemm_hbm_frac"] = round(fig["touched_weight_bytes"] / (gemm * 1e-3)
+                                             / (PEAK_HBM_GBS * 1e9), 4)
+        fig["timing"] = (f"median of {iters} hipEvent-timed layers, L2 and MALL flushed "
+                         "between them")
+    print(f"[bench] {name}: {fig} (inputs {t_in:.1f}s)", file=sys.stderr, flush=True)
+    del x, W, li
+    torch.cuda.empty_cache()
+    return fig
+
+
+def host_info():
+    """CPU model, visible cores and the BLAS numpy calls."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu": model, "cores_visible": len(os.sched_getaffinity(0)), "blas": blas}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
-              "(multi-GPU expert parallelism is not implemented; the library runs one GPU)", file=sys.stderr)
+              "(multi-GPU expert parallelism is not implemented; the library runs one GPU)",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
     from moe_inputs import NAMED
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload != "all":
+        if args.workload not in WORKLOADS:
+            sys.exit(f"bench.py: unknown workload {args.workload}; one of {', '.join(WORKLOADS)}")
+        fig = run_workload(args.workload, args.steps, args.warmup, args.decode_iters)
+        print(json.dumps({"workload": args.workload, **fig}), flush=True)
+        return
+
     cfg = NAMED["mixtral"]
     T, k = 4096, cfg.k
     t_in = time.perf_counter()
@@ -382,18 +535,30 @@ def main():
     flops_down = 2.0 * cfg.d * cfg.ffn * T * k
     flops_layer = cfg.flops(T)
     up_tf = flops_up / (per["expert_up"] * 1e-3) / 1e12
+    down_tf = flops_down / (per["expert_down"] * 1e-3) / 1e12
     gemm_tf = (flops_up + flops_down) / ((per["expert_up"] + per["expert_down"]) * 1e-3) / 1e12
 
-    # decode leg: same layer, first 16 tokens
+    configs = {"mixtral_t4096": layer_figures(cfg, T, wall * 1e3, counts, per)}
+    configs["mixtral_t4096"]["timing"] = "the headline steps (wall clock), per-kernel hipEvents"
+    # decode leg: same layer and weights, first 16 tokens
     dec = None
     if not args.no_decode:
         dec = decode_leg(cfg, x, W, k, args.decode_iters)
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+        configs["mixtral_t16"] = dec.pop("figures")
 
     variants = None
     if args.variants:
         variants = time_variants(cfg, x, W, k, args.steps)
         print(f"[bench] variants: {variants}", file=sys.stderr, flush=True)
+    del x, W
+    torch.cuda.empty_cache()
+
+    for name in WORKLOADS:
+        if name.startswith("mixtral"):
+            continue
+        configs[name] = run_workload(name, min(args.steps, 20), min(args.warmup, 5),
+                                     args.decode_iters)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -412,17 +577,24 @@ def main():
                      "achieved": round(up_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(up_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic("expert_up_mixtral_t4096"),
+                     "traffic_source": "stored rocprofv3 FETCH_SIZE + WRITE_SIZE record "
+                                       "(profiles/traffic.json), null unless taken on this "
+                                       "kernel source",
                      "avg_launch_ms": round(per["expert_up"], 4),
                      "algorithmic_flops_per_launch": flops_up},
+        "grouped_gemm": {"frac_mfma": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+                         "up_frac_mfma": round(up_tf / PEAK_BF16_TFLOPS, 4),
+                         "down_frac_mfma": round(down_tf / PEAK_BF16_TFLOPS, 4),
+                         "down_traffic": stored_traffic("expert_down_mixtral_t4096")},
         "grouped_gemm_frac_mfma": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
         "layer_tflops": round(flops_layer / (layer * 1e-3) / 1e12, 2),
         "kernels_ms": {kname: round(v, 4) for kname, v in per.items()},
         "expert_counts": [int(c) for c in counts],
         "decode": dec,
+        "configs": configs,
         "cpu_baseline": cpu,
         **({"variants": variants} if variants is not None else {}),
-        "host": {"cpu": platform.processor() or platform.machine(),
-                 "cores_visible": len(os.sched_getaffinity(0))},
+        "host": host_info(),
     }
     print(json.dumps(line), flush=True)
 

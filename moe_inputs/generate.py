@@ -40,6 +40,7 @@ from .configs import MoEConfig
 X, W_ROUTER, W_UP, W_GATE, W_DOWN, WS_UP, WS_GATE, WS_DOWN, BIAS = range(9)
 MX_UP, MX_GATE, MX_DOWN = range(9, 12)
 MX8_UP, MX8_GATE, MX8_DOWN = range(12, 15)
+MX8_FULL = 15
 # rms of the E2M1 values when all 16 codes are equally likely: the values are
 # 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, sqrt(68.5 / 8)
 _E2M1_RMS = 2.9261
@@ -203,6 +204,16 @@ def _mx8_draw(cfg: MoEConfig, tensor_id: int, expert_id: int, rows: int, cols: i
     base = int(round(127 + np.log2(std / _E4M3_RMS)))
     scales = (base + rng.integers(-1, 2, size=(rows, cols // 32))).astype(np.uint8)
     return codes.astype(np.uint8), scales
+
+
+def mx8_full_range_codes(cfg: MoEConfig, shape: Tuple[int, ...], tensor: int) -> np.ndarray:
+    """E4M3 code bytes drawn uniformly over the 254 codes that are not NaN
+    (0x7F and 0xFF excluded), every exponent field included; ``tensor``
+    (0, 1, 2 for up, gate, down) keys the stream."""
+    rng = _rng(cfg, MX8_FULL, tensor)
+    v = rng.integers(0, 254, size=shape, dtype=np.int64)
+    v = v + (v >= 0x7F)          # skip 0x7F
+    return v.astype(np.uint8)    # 254 -> 0xFF is never drawn: top value is 0xFE
 
 
 def mxfp8_expert_weights(cfg: MoEConfig, e: int, shared: bool = False):

@@ -54,6 +54,30 @@ def check_routing(idx_gpu, w_gpu, counts_gpu, ref):
     return werr
 
 
+def h_rounding_bound(X: np.ndarray, ref, groups, E: int, d: int) -> np.ndarray:
+    """Per element of y: 2^-8 * (sum over kept pairs of |w| |h| @ |W_down|^T,
+    plus the shared experts' |h| @ |W_down|^T), from fp64 h.  ``groups``
+    yields (g, (W_up, W_gate, W_down)) as float64 arrays, routed experts as
+    g < E and shared experts as g >= E.  The down projection takes h rounded
+    to bf16 (2^-9 relative); this is twice that rounding carried through the
+    combine."""
+    import oracle
+    b = np.zeros((X.shape[0], d))
+    for g, (wu, wg, wd) in groups:
+        if g < E:
+            t, j = np.nonzero((ref.idx == g) & ref.keep)
+            scale = np.abs(ref.w[t, j])
+        else:
+            t = np.arange(X.shape[0])
+            scale = np.ones(X.shape[0])
+        if t.size == 0:
+            continue
+        Xg = X[t]
+        H = oracle.silu(Xg @ wg.T) * (Xg @ wu.T)
+        np.add.at(b, t, scale[:, None] * (np.abs(H) @ np.abs(wd).T))
+    return 2.0 ** -8 * b
+
+
 def sample_tokens(T: int, n: int = 24, seed: int = 0) -> np.ndarray:
     if T <= n:
         return np.arange(T)
