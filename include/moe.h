@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -94,7 +94,9 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARG = -1, /* a size, pointer or enum is out of range        */
   MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape the kernels reject    */
   MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than needed  */
-  MOE_ERR_HIP = -4          /* a HIP call or kernel launch failed             */
+  MOE_ERR_HIP = -4,         /* a HIP call or kernel launch failed             */
+  MOE_ERR_TOO_LARGE = -5    /* moe_forward_noalloc: the layer needs more
+                               scratch than MOE_NOALLOC_SCRATCH_BYTES         */
 } moe_status;
 
 /* Which expert-GEMM kernels run.  AUTO picks DECODE when the mean number of
@@ -190,6 +192,34 @@ int moe_forward(const moe_desc* desc, const void* x, const void* w_router,
                 const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
                 int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                 moe_stream stream);
+
+/* Scratch held inside the library for moe_forward_noalloc: 64 MiB per GPU. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results are those of moe_forward without the workspace; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Scratch is a device array of MOE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the first call on a
+ * device looks up that device's copy.  Limit: a layer whose
+ * moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_ERR_TOO_LARGE before any launch.  Decode-sized layers fit, e.g.
+ * d=2880, 128 experts, top-4, ffn 2880 at T=512 (40 MiB); d=4096, 8 experts,
+ * top-2, ffn 14336 at T=256 (45 MiB); d=7168, 256 experts, top-8, ffn 2048
+ * and one shared expert at T=128 (49 MiB).
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind (no kernel reads scratch it has not written in the same call):
+ * calls that overlap on one GPU (on different streams, or from host threads
+ * without ordering) race and give undefined results; order them on one
+ * stream.  MOE_ERR_HIP if the device array cannot be looked up.
+ */
+int moe_forward_noalloc(const moe_desc* desc, const void* x, const void* w_router,
+                        const float* router_bias, const void* w_up, const void* w_gate,
+                        const void* w_down, const void* ws_up, const void* ws_gate,
+                        const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                        int32_t* expert_counts, moe_stream stream);
 
 /* Scale arrays of MXFP4 or MXFP8 expert weights (uint8 E8M0, one per 32 elements
  * along K): up, gate [E,ffn,d/32], down [E,d,ffn/32]; shared-expert

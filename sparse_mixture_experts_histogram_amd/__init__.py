@@ -6,7 +6,7 @@ thin Python binding: PyTorch supplies device memory and the stream.
 """
 from .api import (  # noqa: F401
     MxWeights, Routing, Weights, make_desc, moe_combine, moe_dispatch, moe_experts, moe_forward,
-    moe_forward_mx, moe_forward_timed,
+    moe_forward_mx, moe_forward_noalloc, moe_forward_timed,
     moe_grouped_rows,
     moe_resolve_path, moe_route, moe_validate, moe_workspace_size, workspace,
 )

@@ -18,13 +18,14 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
-          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_TOO_LARGE"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 WEIGHTS_RENORM, WEIGHTS_RAW = 0, 1
 EXPERTS_DENSE, EXPERTS_MXFP4, EXPERTS_MXFP8 = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeDesc(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib():
     V = c_void_p
     L.moe_forward.restype = c_int
     L.moe_forward.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V]
+    L.moe_forward_noalloc.restype = c_int
+    L.moe_forward_noalloc.argtypes = [D, V, V, V, V, V, V, V, V, V, V, V, V, V, V]
     L.moe_forward_mx.restype = c_int
     L.moe_forward_mx.argtypes = [D, V, V, V, V, V, V, V, V, V, POINTER(MoeMxScales), V, V, V, V,
                                  V, c_size_t, V, V]

@@ -155,6 +155,33 @@ def moe_forward(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32, path
     return (y, idx, w, counts) if return_routing else y
 
 
+def moe_forward_noalloc(x: torch.Tensor, W: Weights, k: int, y_dtype=torch.float32,
+                        path: str = "auto", return_routing: bool = False,
+                        routing: Routing = Routing(), y: Optional[torch.Tensor] = None):
+    """moe_forward on the library's own per-GPU scratch (no workspace
+    argument; the C call allocates nothing).  Outputs are allocated here
+    unless ``y`` is given.  Raises MoeError(MOE_ERR_TOO_LARGE) for layers
+    whose workspace exceeds the scratch."""
+    _check_weights(W, x)
+    T = x.shape[0]
+    desc = W.desc(T, k, y_dtype, path, routing)
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, x.shape[1]), dtype=y_dtype, device=dev)
+    idx = w = counts = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((W.w_up.shape[0],), dtype=torch.int32, device=dev)
+    st = _lib.lib().moe_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(W.w_router),
+                                        _ptr(W.bias), _ptr(W.w_up), _ptr(W.w_gate),
+                                        _ptr(W.w_down), _ptr(W.ws_up), _ptr(W.ws_gate),
+                                        _ptr(W.ws_down), _ptr(y), _ptr(idx), _ptr(w),
+                                        _ptr(counts), _stream(dev))
+    _check(st, "moe_forward_noalloc")
+    return (y, idx, w, counts) if return_routing else y
+
+
 @dataclass
 class MxWeights:
     """A layer whose expert weights are MX-format: MXFP4 (uint8 E2M1 code

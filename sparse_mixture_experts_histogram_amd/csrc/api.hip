@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "kernels.h"
 #include "plan.h"
@@ -124,9 +125,57 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
 }  // namespace
 }  // namespace moe
 
+namespace moe {
+namespace {
+
+// Scratch of moe_forward_noalloc.  Each GPU the library runs on holds its own
+// copy (loaded with the code object) until the process ends.  Host code never
+// passes this name to a kernel or a copy: it is a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
 using namespace moe;
 
 extern "C" {
+
+int moe_forward_noalloc(const moe_desc* d, const void* x, const void* w_router,
+                        const float* router_bias, const void* w_up, const void* w_gate,
+                        const void* w_down, const void* ws_up, const void* ws_gate,
+                        const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                        int32_t* expert_counts, moe_stream stream) {
+  Plan P;
+  int st = make_plan(d, &P);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (P.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(d, x, w_router, router_bias, w_up, w_gate, w_down, ws_up, ws_gate,
+                      ws_down, nullptr, y, topk_idx, topk_w, expert_counts, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
 
 int moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* router_bias,
                 const void* w_up, const void* w_gate, const void* w_down, const void* ws_up,

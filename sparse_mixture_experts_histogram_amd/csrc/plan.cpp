@@ -225,6 +225,9 @@ const char* moe_status_str(int s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by the kernels";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the layer needs more scratch than moe_forward_noalloc holds "
+             "(MOE_NOALLOC_SCRATCH_BYTES); use moe_forward with a workspace";
     default: return "unknown moe_status";
   }
 }

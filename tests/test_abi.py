@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
             "moe_workspace_size", "moe_validate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == _lib.ABI_VERSION == 3
+    assert L.moe_abi_version() == _lib.ABI_VERSION == 4
 
 
 def test_desc_struct_size():
@@ -139,3 +139,22 @@ def test_zero_tokens_touch_nothing():
     assert L.moe_forward(ctypes.byref(d), *([None] * 13), None, 0, None) == OK
     assert L.moe_route(ctypes.byref(d), None, None, None, None, None, None, 0, None) == OK
     assert L.moe_combine(ctypes.byref(d), None, None, None, None, None, None) == OK
+
+
+def test_noalloc_host_checks():
+    """moe_forward_noalloc's checks run on the host before it touches a
+    device: an invalid descriptor, an empty batch, and a layer whose
+    workspace exceeds the library's scratch (MOE_ERR_TOO_LARGE)."""
+    L = _lib.lib()
+    args = [None] * 14
+    assert L.moe_forward_noalloc(desc(k=0), *args) == INVALID
+    assert L.moe_forward_noalloc(desc(T=0), *args) == OK
+    big = desc(T=4096, d=4096, E=8, k=2, ffn=14336)
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(big, ctypes.byref(n)) == OK
+    assert n.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(big, *args) == -5
+    assert b"MOE_ERR_TOO_LARGE" in L.moe_status_str(-5)
+    small = desc(T=512, d=2880, E=128, k=4, ffn=2880)
+    assert L.moe_workspace_size(small, ctypes.byref(n)) == OK
+    assert n.value <= _lib.NOALLOC_SCRATCH_BYTES
