@@ -466,6 +466,20 @@ def run_workload(name, steps, warmup, iters):
     return fig
 
 
+def copy_check(mb):
+    """One elementwise kernel that reads and writes exactly `mb` megabytes
+    (after a fill that writes them): a kernel of known traffic for scaling
+    rocprofv3's FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    n = mb * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def host_info():
     """CPU model, visible cores and the BLAS numpy calls."""
     model = platform.processor() or platform.machine()
@@ -500,6 +514,8 @@ def main():
     from moe_inputs import NAMED
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_check:
+        copy_check(args.copy_check)
     if args.workload != "all":
         if args.workload not in WORKLOADS:
             sys.exit(f"bench.py: unknown workload {args.workload}; one of {', '.join(WORKLOADS)}")
@@ -515,15 +531,6 @@ def main():
     print(f"[bench] inputs ready in {time.perf_counter() - t_in:.1f}s", file=sys.stderr,
           flush=True)
 
-    if args.copy_check:
-        # one elementwise kernel that reads and writes exactly MB megabytes
-        n = args.copy_check * 1024 * 1024 // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.add(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
     if args.no_prefill:
         dec = decode_leg(cfg, x, W, k, args.decode_iters)
         print(json.dumps({"decode_only": dec}), flush=True)

@@ -8,12 +8,18 @@
 // When the down GEMM split K (into 2 to 4 ranges), each expert output row is
 // the sum of its partial rows, added here in range order.
 // HBM-bound: it reads (k + n_shared) float32 rows (per K range) and writes one
-// row per token; each workgroup handles one token with 16-byte accesses.
+// row per token, with 16-byte accesses.
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
+// Workgroup (t, q) handles columns [1024 q, 1024 q + 1024) of token t, one
+// float4 per thread.  The rows of a token are loaded in batches of
+// kCombineBatch (all loads of a batch issued before the first add), so a
+// token costs about ceil((k + n_shared) / kCombineBatch) memory round trips
+// rather than one per row; the adds keep the order above.
+constexpr int kCombineBatch = 8;
 template <bool Y_BF16, int NP>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
                                                       int64_t part_stride,
@@ -31,46 +37,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     rows[threadIdx.x] = offsets[E + threadIdx.x - k] + t;
   }
   __syncthreads();
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c >= (d >> 2)) return;
   // expert output row r: its NP partial K-range sums, added in order
-  auto row4 = [&](int r, int c) {
-    float4 v = ((const float4*)(out + (int64_t)r * d))[c];
+  auto row4 = [&](int r) {
+    float4 v[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+      v[q] = ((const float4*)(out + q * part_stride + (int64_t)r * d))[c];
 #pragma unroll
     for (int q = 1; q < NP; ++q) {
-      const float4 u = ((const float4*)(out + q * part_stride + (int64_t)r * d))[c];
-      v.x += u.x;
-      v.y += u.y;
-      v.z += u.z;
-      v.w += u.w;
+      v[0].x += v[q].x;
+      v[0].y += v[q].y;
+      v[0].z += v[q].z;
+      v[0].w += v[q].w;
     }
-    return v;
+    return v[0];
   };
-  const int d4 = d >> 2;
-  for (int c = threadIdx.x; c < d4; c += blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      if (rows[j] < 0) continue;  // pair dropped by an expert capacity
-      const float4 v = row4(rows[j], c);
-      const float wj = wts[j];
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
+  const int n = k + n_sh;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
+    float4 v[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int j = j0 + i;
+      const int r = j < n ? rows[j] : -1;  // -1: past the end, or dropped by a capacity
+      v[i] = r >= 0 ? row4(r) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int s = 0; s < n_sh; ++s) {
-      const float4 v = row4(rows[k + s], c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int j = j0 + i;
+      if (j >= n) break;
+      if (j < k) {
+        if (rows[j] < 0) continue;  // pair dropped by an expert capacity
+        const float wj = wts[j];
+        acc.x = fmaf(wj, v[i].x, acc.x);
+        acc.y = fmaf(wj, v[i].y, acc.y);
+        acc.z = fmaf(wj, v[i].z, acc.z);
+        acc.w = fmaf(wj, v[i].w, acc.w);
+      } else {  // shared experts, weight one
+        acc.x += v[i].x;
+        acc.y += v[i].y;
+        acc.z += v[i].z;
+        acc.w += v[i].w;
+      }
     }
-    if (Y_BF16) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-      ((uint2*)((uint16_t*)y + (int64_t)t * d))[c] = pk;
-    } else {
-      ((float4*)((float*)y + (int64_t)t * d))[c] = acc;
-    }
+  }
+  if (Y_BF16) {
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+    pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+    ((uint2*)((uint16_t*)y + (int64_t)t * d))[c] = pk;
+  } else {
+    ((float4*)((float*)y + (int64_t)t * d))[c] = acc;
   }
 }
 
@@ -78,7 +97,7 @@ hipError_t launch_combine(const Plan& P, const float* out, int nparts, int64_t p
                           const float* w, const int32_t* slot_row, const int32_t* offsets,
                           void* y, hipStream_t s) {
   const moe_desc& D = P.desc;
-  const dim3 grid((unsigned)D.T), block(256);
+  const dim3 grid((unsigned)D.T, (unsigned)((D.d / 4 + 255) / 256)), block(256);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, out, part_stride, w, slot_row, offsets, D.d, D.k,
                        D.E, D.n_shared, y);

@@ -8,8 +8,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
     int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
     int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
     TileCfg cd) {
-  dispatch_body(idx, blk_hist, blk_rank, T, k, E, n_sh, nblk, cap, counts, offsets, sorted_token,
-                slot_row, tiles_up, cu, tiles_down, cd);
+  dispatch_body<false>(idx, blk_hist, blk_rank, T, k, E, n_sh, nblk, cap, counts, offsets,
+                       sorted_token, slot_row, tiles_up, cu, tiles_down, cd);
 }
 
 // Tile schedules from existing group offsets (used when the expert step is

@@ -122,8 +122,12 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
 }
 
 // The whole dispatch, run by one workgroup of kDispatchThreads threads.
-// (No __restrict__: in the router's fused form idx, blk_hist and blk_rank
-// are LDS arrays the same workgroup has just written.)
+// ONE_BLOCK: a single token block whose histogram and ranks the same
+// workgroup has just computed (the router's fused form: idx, blk_hist and
+// blk_rank are LDS arrays, hence no __restrict__); the block's exclusive
+// offsets are then all zero and there is no column scan.  Pair indices fit
+// in 32 bits (the descriptor check bounds T * (k + n_shared) below 2^31).
+template <bool ONE_BLOCK>
 __device__ __forceinline__ void dispatch_body(
     const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
     int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
@@ -139,6 +143,15 @@ __device__ __forceinline__ void dispatch_body(
   const int tid = threadIdx.x;
   const int G = E + n_sh;
 
+  if constexpr (ONE_BLOCK) {
+    if (tid < E) {
+      const int run = blk_hist[tid];
+      gsize[tid] = min(run, cap);
+      counts[tid] = run;
+    }
+    if (tid >= E && tid < G) gsize[tid] = T;
+    __syncthreads();
+  } else {
   // 1. column scans of the block histogram: expert e's column is split into
   // S segments of about kBatch blocks (at most kDispatchThreads / Ep), one
   // thread each; a thread per expert then walks the S segment sums in order.
@@ -192,6 +205,7 @@ __device__ __forceinline__ void dispatch_body(
   }
   if (tid >= E && tid < G) gsize[tid] = T;
   __syncthreads();
+  }
 
   // 2. group offsets; 3. row-tile bases of both schedules
   int total;
@@ -215,27 +229,39 @@ __device__ __forceinline__ void dispatch_body(
   // 4. stable placement of the routed pairs, kPlace pairs per thread at a
   // time (their index and rank loads, then their block-offset loads, are
   // each one batch)
+  const int pairs = T * k;
+  if constexpr (ONE_BLOCK) {
+    for (int p = tid; p < pairs; p += blockDim.x) {
+      const int e = idx[p], r = blk_rank[p];
+      if (r < cap) {
+        slot_row[p] = goff[e] + r;
+        sorted_token[goff[e] + r] = p / k;
+      } else {
+        slot_row[p] = -1;
+      }
+    }
+  } else {
   constexpr int kPlace = 8;
-  const int64_t pairs = (int64_t)T * k;
-  for (int64_t p0 = tid; p0 < pairs; p0 += (int64_t)kPlace * blockDim.x) {
+  const uint32_t uk = (uint32_t)k;
+  for (int p0 = tid; p0 < pairs; p0 += kPlace * kDispatchThreads) {
     int ee[kPlace], rk[kPlace], off[kPlace];
 #pragma unroll
     for (int i = 0; i < kPlace; ++i) {
-      const int64_t p = p0 + (int64_t)i * blockDim.x;
+      const int p = p0 + i * kDispatchThreads;
       ee[i] = p < pairs ? idx[p] : 0;
       rk[i] = p < pairs ? blk_rank[p] : 0;
     }
 #pragma unroll
     for (int i = 0; i < kPlace; ++i) {
-      const int64_t p = p0 + (int64_t)i * blockDim.x;
-      const int b = (int)(p / k) / kRouterTokens;
-      off[i] = p < pairs ? blk_hist[(int64_t)b * E + ee[i]] : 0;
+      const int p = p0 + i * kDispatchThreads;
+      const int b = (int)((uint32_t)p / uk) / kRouterTokens;
+      off[i] = p < pairs ? blk_hist[b * E + ee[i]] : 0;
     }
 #pragma unroll
     for (int i = 0; i < kPlace; ++i) {
-      const int64_t p = p0 + (int64_t)i * blockDim.x;
+      const int p = p0 + i * kDispatchThreads;
       if (p >= pairs) continue;
-      const int t = (int)(p / k);
+      const int t = (int)((uint32_t)p / uk);
       const int r = off[i] + rk[i];  // position in the expert's run
       if (r < cap) {
         slot_row[p] = goff[ee[i]] + r;
@@ -244,6 +270,7 @@ __device__ __forceinline__ void dispatch_body(
         slot_row[p] = -1;
       }
     }
+  }
   }
   // 5. shared groups: identity rows
   for (int s = 0; s < n_sh; ++s)

@@ -360,6 +360,13 @@ struct FusedDispatch {
 // fence, which writes back and invalidates L2 and measured slower than the
 // separate launch.)  kDispatchThreads threads; dynamic LDS: [16][ld] floats,
 // then sel[16*k].
+// EPL = experts per lane of the selection (E <= 64 EPL); FUSED: the single
+// token block's workgroup also runs the dispatch.  Each (EPL, FUSED) pair is
+// its own kernel so that a launch carries only the code it runs: these
+// kernels run once per layer on one or a few workgroups, and a kernel holding
+// every selection width and both tails was large enough for instruction
+// fetch to dominate its time.
+template <int EPL, bool FUSED>
 __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     const float* __restrict__ part, int64_t plane, const float* __restrict__ bias, int mode, int T,
     int E, int k, int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist,
@@ -380,20 +387,42 @@ __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     lds[(i / ep) * ld + i % ep] = s;
   }
   __syncthreads();
-  if (!fd.counts || nblk != 1) {
-    router_tail_dispatch(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, blk_hist,
-                         blk_rank);
-    return;
+  if constexpr (!FUSED) {
+    router_tail<EPL>(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out,
+                     blk_hist + (int64_t)blockIdx.x * E, blk_rank + (int64_t)t0 * k);
+  } else {
+    // Fused dispatch (one token block, t0 = 0): the block's expert ids (sel,
+    // in pair order), histogram and ranks stay in LDS for the dispatch
+    // instead of a round trip through global memory.
+    __shared__ int32_t f_hist[kMaxExperts];
+    __shared__ int32_t f_rank[kRouterTokens * kMaxTopK];
+    router_tail<EPL>(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, f_hist, f_rank);
+    __syncthreads();
+    dispatch_body<true>(sel, f_hist, f_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts,
+                        fd.offsets, fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu,
+                        fd.tiles_down, fd.cd);
   }
-  // Fused dispatch (one token block, t0 = 0): the block's expert ids (sel,
-  // in pair order), histogram and ranks stay in LDS for the dispatch instead
-  // of a round trip through global memory.
-  __shared__ int32_t f_hist[kMaxExperts];
-  __shared__ int32_t f_rank[kRouterTokens * kMaxTopK];
-  router_tail_to(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, f_hist, f_rank);
-  __syncthreads();
-  dispatch_body(sel, f_hist, f_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts, fd.offsets,
-                fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu, fd.tiles_down, fd.cd);
+}
+
+// The finish kernel for E experts (and the fused dispatch or not).
+template <bool FUSED>
+hipError_t launch_finish(dim3 grid, size_t lds, hipStream_t s, const float* part, int64_t plane,
+                         const float* bias, int mode, int T, int E, int k, int nblk, int nsplit,
+                         int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
+                         FusedDispatch fd) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kDispatchThreads), lds, s, part, plane, bias, mode, T, E,
+                       k, nblk, nsplit, idx, w, blk_hist, blk_rank, fd);
+  };
+  if (E <= 64)
+    go(router_finish_kernel<1, FUSED>);
+  else if (E <= 128)
+    go(router_finish_kernel<2, FUSED>);
+  else if (E <= 256)
+    go(router_finish_kernel<4, FUSED>);
+  else
+    go(router_finish_kernel<8, FUSED>);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -484,11 +513,10 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
       partial(router_wide_partial_kernel<8>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
-                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
-                       (int64_t)ngroups * P.rwide * ep, bias, P.route_mode, (int)D.T, D.E, D.k,
-                       (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, FusedDispatch{});
-    return hipGetLastError();
+    return launch_finish<false>(grid, (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
+                                (int64_t)ngroups * P.rwide * ep, bias, P.route_mode, (int)D.T, D.E,
+                                D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank,
+                                FusedDispatch{});
   }
   if (P.rsplit > 1) {
     FusedDispatch fd{};
@@ -512,11 +540,13 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
       partial(router_partial_kernel<8, NW>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(router_finish_kernel, grid, dim3(kDispatchThreads),
-                       (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
-                       (int64_t)P.nblk * kRouterTokens * ep, bias, P.route_mode, (int)D.T, D.E,
-                       D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
-    return hipGetLastError();
+    const size_t flds = (size_t)kRouterTokens * ld * 4 + sel_bytes;
+    const int64_t plane = (int64_t)P.nblk * kRouterTokens * ep;
+    if (fd.counts)
+      return launch_finish<true>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
+                                 D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
+    return launch_finish<false>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
+                                D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
   }
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, s, xb, wb, bias, P.route_mode, (int)D.T,
