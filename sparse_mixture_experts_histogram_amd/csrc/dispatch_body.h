@@ -86,10 +86,15 @@ __device__ __forceinline__ int group_of_slot(const int* mbase, int G, int mL) {
   }
   return lo;
 }
+// Entries first, first + stride, ... of the schedule are written by the
+// calling thread (first = thread index and stride = block size for one
+// workgroup; a global thread index and the grid's thread count when several
+// workgroups share the work); the thread with first == 0 writes the header.
+// Every workgroup builds the whole row-tile table in its own LDS.
 __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
-                            TileCfg c, Tile* tiles, int* rt_tab) {
+                            TileCfg c, Tile* tiles, int* rt_tab, int first, int stride) {
   const int total = mtot * c.n_tiles;
-  if (threadIdx.x == 0) tiles[0] = Tile{total, mtot, c.n_tiles, 0};
+  if (first == 0) tiles[0] = Tile{total, mtot, c.n_tiles, 0};
   const bool tab = mtot <= kRowTileTable;
   if (tab) {
     for (int m = threadIdx.x; m < mtot; m += blockDim.x) rt_tab[m] = group_of_slot(mbase, G, m);
@@ -98,7 +103,7 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
   // Row-tile list only: entry 1 + i is row tile i (in group order); a kernel
   // reads entry L as row tile L % mtot of column tile L / mtot.
   const int entries = c.row_list ? mtot : total;
-  for (int L = threadIdx.x; L < entries; L += blockDim.x) {
+  for (int L = first; L < entries; L += stride) {
     const int mL = c.row_list ? L : L / c.n_tiles;  // row tile "slot"
     const int g = tab ? rt_tab[mL] : group_of_slot(mbase, G, mL);
     if (c.row_list) {
@@ -121,53 +126,27 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
   if (tab) __syncthreads();  // the table is free again
 }
 
-// The whole dispatch, run by one workgroup of kDispatchThreads threads.
-// ONE_BLOCK: a single token block whose histogram and ranks the same
-// workgroup has just computed (the router's fused form: idx, blk_hist and
-// blk_rank are LDS arrays, hence no __restrict__); the block's exclusive
-// offsets are then all zero and there is no column scan.  Pair indices fit
-// in 32 bits (the descriptor check bounds T * (k + n_shared) below 2^31).
-template <bool ONE_BLOCK>
-__device__ __forceinline__ void dispatch_body(
-    const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
-    int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
-    int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
-    TileCfg cd) {
-  __shared__ int part[kDispatchThreads];
-  __shared__ int scan_buf[kDispatchThreads / 64];
-  __shared__ int goff[kMaxGroups + 1];
-  __shared__ int gsize[kMaxGroups];
-  __shared__ int mb_up[kMaxGroups + 1];
-  __shared__ int mb_dn[kMaxGroups + 1];
-  __shared__ int rt_tab[kRowTileTable];
-  const int tid = threadIdx.x;
-  const int G = E + n_sh;
-
-  if constexpr (ONE_BLOCK) {
-    if (tid < E) {
-      const int run = blk_hist[tid];
-      gsize[tid] = min(run, cap);
-      counts[tid] = run;
-    }
-    if (tid >= E && tid < G) gsize[tid] = T;
-    __syncthreads();
-  } else {
-  // 1. column scans of the block histogram: expert e's column is split into
-  // S segments of about kBatch blocks (at most kDispatchThreads / Ep), one
-  // thread each; a thread per expert then walks the S segment sums in order.
-  // (S is not simply kDispatchThreads / Ep: with few blocks that serial walk
-  // over mostly empty segments was most of the dispatch time.)
+// Step 1 for experts [e0, e0 + nE) (nE <= kDispatchThreads), by one
+// workgroup: each expert's column of block counts is split into S segments
+// of about kBatch blocks (at most kDispatchThreads / Ep), one thread each; a
+// thread per expert then walks the S segment sums in order.  Writes the
+// expert totals to counts[] and to gsize[] (LDS, capped at cap; indexed from
+// e0), and each block's exclusive offset over the column in place.  (S is
+// not simply kDispatchThreads / Ep: with few blocks that serial walk over
+// mostly empty segments was most of the dispatch time.  Loads go in batches
+// of kBatch independent loads: one memory round trip per block was most of
+// the dispatch time for many blocks and experts.)
+__device__ __forceinline__ void column_scan(int32_t* blk_hist, int nblk, int E, int e0, int nE,
+                                            int cap, int32_t* counts, int* gsize, int* part) {
   constexpr int kBatch = 32;
+  const int tid = threadIdx.x;
   int Ep = 1;
-  while (Ep < E) Ep <<= 1;
+  while (Ep < nE) Ep <<= 1;
   const int S = min(kDispatchThreads / Ep, max(1, (nblk + kBatch - 1) / kBatch));
-  const int e = tid % Ep, seg = tid / Ep;
+  const int el = tid % Ep, seg = tid / Ep, e = e0 + el;
   const int b0 = seg < S ? (int)((int64_t)seg * nblk / S) : 0;
   const int b1 = seg < S ? (int)((int64_t)(seg + 1) * nblk / S) : 0;
-  // (Loads go in batches of kBatch independent loads: a thread walks up to
-  // nblk / S blocks, and one memory round trip per block was most of the
-  // dispatch time for many blocks and experts.)
-  if (e < E && seg < S) {
+  if (el < nE && seg < S) {
     int s = 0;
     for (int b = b0; b < b1; b += kBatch) {
       int v[kBatch];
@@ -176,10 +155,10 @@ __device__ __forceinline__ void dispatch_body(
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) s += v[i];
     }
-    part[seg * Ep + e] = s;
+    part[seg * Ep + el] = s;
   }
   __syncthreads();
-  if (tid < E) {
+  if (tid < nE) {
     int run = 0;
     for (int q = 0; q < S; ++q) {
       const int v = part[q * Ep + tid];
@@ -187,11 +166,11 @@ __device__ __forceinline__ void dispatch_body(
       run += v;
     }
     gsize[tid] = min(run, cap);
-    counts[tid] = run;
+    counts[e0 + tid] = run;
   }
   __syncthreads();
-  if (e < E && seg < S) {
-    int run = part[seg * Ep + e];
+  if (el < nE && seg < S) {
+    int run = part[seg * Ep + el];
     for (int b = b0; b < b1; b += kBatch) {
       int v[kBatch];
 #pragma unroll
@@ -203,10 +182,26 @@ __device__ __forceinline__ void dispatch_body(
       }
     }
   }
-  if (tid >= E && tid < G) gsize[tid] = T;
-  __syncthreads();
-  }
+}
 
+// Steps 2-5 given the group sizes gsize[G] in LDS (routed experts capped at
+// the capacity, then the shared groups): group offsets and row-tile bases in
+// LDS, then the schedules, the placement of the pairs and the shared rows,
+// over thread range (first, stride) as in build_tiles.  ONE_BLOCK: the
+// block offsets are zero (a single token block), so blk_hist is not read.
+template <bool ONE_BLOCK>
+__device__ __forceinline__ void layout_and_place(
+    const int32_t* idx, const int32_t* blk_hist, const int32_t* blk_rank, int T, int k, int E,
+    int n_sh, int cap, const int* gsize, int32_t* offsets, int32_t* sorted_token,
+    int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down, TileCfg cd, int first,
+    int stride) {
+  __shared__ int scan_buf[kDispatchThreads / 64];
+  __shared__ int goff[kMaxGroups + 1];
+  __shared__ int mb_up[kMaxGroups + 1];
+  __shared__ int mb_dn[kMaxGroups + 1];
+  __shared__ int rt_tab[kRowTileTable];
+  const int tid = threadIdx.x;
+  const int G = E + n_sh;
   // 2. group offsets; 3. row-tile bases of both schedules
   int total;
   const int sz = tid < G ? gsize[tid] : 0;
@@ -222,16 +217,16 @@ __device__ __forceinline__ void dispatch_body(
   const int exd = block_excl_scan(md, scan_buf, &mtot_d);
   if (tid <= G) mb_dn[tid] = tid < G ? exd : mtot_d;
   __syncthreads();
-  for (int g = tid; g <= G; g += blockDim.x) offsets[g] = goff[g];
-  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab);
-  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab);
+  for (int g = first; g <= G; g += stride) offsets[g] = goff[g];
+  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab, first, stride);
+  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab, first, stride);
 
   // 4. stable placement of the routed pairs, kPlace pairs per thread at a
   // time (their index and rank loads, then their block-offset loads, are
   // each one batch)
   const int pairs = T * k;
   if constexpr (ONE_BLOCK) {
-    for (int p = tid; p < pairs; p += blockDim.x) {
+    for (int p = first; p < pairs; p += stride) {
       const int e = idx[p], r = blk_rank[p];
       if (r < cap) {
         slot_row[p] = goff[e] + r;
@@ -241,40 +236,72 @@ __device__ __forceinline__ void dispatch_body(
       }
     }
   } else {
-  constexpr int kPlace = 8;
-  const uint32_t uk = (uint32_t)k;
-  for (int p0 = tid; p0 < pairs; p0 += kPlace * kDispatchThreads) {
-    int ee[kPlace], rk[kPlace], off[kPlace];
+    constexpr int kPlace = 8;
+    const uint32_t uk = (uint32_t)k;
+    for (int p0 = first; p0 < pairs; p0 += kPlace * stride) {
+      int ee[kPlace], rk[kPlace], off[kPlace];
 #pragma unroll
-    for (int i = 0; i < kPlace; ++i) {
-      const int p = p0 + i * kDispatchThreads;
-      ee[i] = p < pairs ? idx[p] : 0;
-      rk[i] = p < pairs ? blk_rank[p] : 0;
-    }
+      for (int i = 0; i < kPlace; ++i) {
+        const int p = p0 + i * stride;
+        ee[i] = p < pairs ? idx[p] : 0;
+        rk[i] = p < pairs ? blk_rank[p] : 0;
+      }
 #pragma unroll
-    for (int i = 0; i < kPlace; ++i) {
-      const int p = p0 + i * kDispatchThreads;
-      const int b = (int)((uint32_t)p / uk) / kRouterTokens;
-      off[i] = p < pairs ? blk_hist[b * E + ee[i]] : 0;
-    }
+      for (int i = 0; i < kPlace; ++i) {
+        const int p = p0 + i * stride;
+        const int b = (int)((uint32_t)p / uk) / kRouterTokens;
+        off[i] = p < pairs ? blk_hist[(int64_t)b * E + ee[i]] : 0;
+      }
 #pragma unroll
-    for (int i = 0; i < kPlace; ++i) {
-      const int p = p0 + i * kDispatchThreads;
-      if (p >= pairs) continue;
-      const int t = (int)((uint32_t)p / uk);
-      const int r = off[i] + rk[i];  // position in the expert's run
-      if (r < cap) {
-        slot_row[p] = goff[ee[i]] + r;
-        sorted_token[goff[ee[i]] + r] = t;
-      } else {
-        slot_row[p] = -1;
+      for (int i = 0; i < kPlace; ++i) {
+        const int p = p0 + i * stride;
+        if (p >= pairs) continue;
+        const int t = (int)((uint32_t)p / uk);
+        const int r = off[i] + rk[i];  // position in the expert's run
+        if (r < cap) {
+          slot_row[p] = goff[ee[i]] + r;
+          sorted_token[goff[ee[i]] + r] = t;
+        } else {
+          slot_row[p] = -1;
+        }
       }
     }
   }
-  }
   // 5. shared groups: identity rows
   for (int s = 0; s < n_sh; ++s)
-    for (int t = tid; t < T; t += blockDim.x) sorted_token[goff[E + s] + t] = t;
+    for (int t = first; t < T; t += stride) sorted_token[goff[E + s] + t] = t;
+}
+
+// The whole dispatch, run by one workgroup of kDispatchThreads threads.
+// ONE_BLOCK: a single token block whose histogram and ranks the same
+// workgroup has just computed (the router's fused form: idx, blk_hist and
+// blk_rank are LDS arrays, hence no __restrict__); the block's exclusive
+// offsets are then all zero and there is no column scan.  Pair indices fit
+// in 32 bits (the descriptor check bounds T * (k + n_shared) below 2^31).
+template <bool ONE_BLOCK>
+__device__ __forceinline__ void dispatch_body(
+    const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
+    int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
+    int32_t* sorted_token, int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down,
+    TileCfg cd) {
+  __shared__ int part[kDispatchThreads];
+  __shared__ int gsize[kMaxGroups];
+  const int tid = threadIdx.x;
+  const int G = E + n_sh;
+  if constexpr (ONE_BLOCK) {
+    if (tid < E) {
+      const int run = blk_hist[tid];
+      gsize[tid] = min(run, cap);
+      counts[tid] = run;
+    }
+  } else {
+    column_scan(blk_hist, nblk, E, 0, E, cap, counts, gsize, part);
+  }
+  if (tid >= E && tid < G) gsize[tid] = T;
+  __syncthreads();
+  layout_and_place<ONE_BLOCK>(idx, blk_hist, blk_rank, T, k, E, n_sh, cap, gsize, offsets,
+                              sorted_token, slot_row, tiles_up, cu, tiles_down, cd, tid,
+                              kDispatchThreads);
 }
 
 static inline TileCfg tile_cfg(const GemmShape& s) {

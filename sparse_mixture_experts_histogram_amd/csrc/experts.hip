@@ -110,14 +110,30 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t s
                                              off[i], soff, 0, AUX);
 }
 
+// dma_tile where block i reads through `dead` (a size-0 descriptor: zeros, no
+// memory traffic) unless bit i of `live` is set.
+template <int NBLK, int NW, int AUX = 0>
+__device__ __forceinline__ void dma_tile_live(__amdgpu_buffer_rsrc_t rsrc,
+                                              __amdgpu_buffer_rsrc_t dead, uint32_t live,
+                                              uint32_t soff, const uint32_t* off, uint16_t* lds,
+                                              int wave) {
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(((live >> i) & 1u) ? rsrc : dead,
+                                             LDS_PTR(lds + (wave + NW * i) * 512), 16, off[i],
+                                             soff, 0, AUX);
+}
+
 // Buffer descriptor of `bytes` bytes at p (raw buffer: no stride, no format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-constexpr int kPolW = 0, kPolX = 0;  // cache policy bits of the weight / token bursts
+constexpr int kPolX = 0;  // cache policy bits of the token bursts
 constexpr int kSpread = 2;            // k-steps of a slab over which its DMAs are issued
-template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX>
+// POLW: cache policy bits of the weight bursts (0, or non-temporal when each
+// weight tile is read by a single row tile).
+template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX, int POLW>
 __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WROWS = UPGATE ? 2 * BN : BN;        // weight rows in the tile
   constexpr int NWN = BN / WN, NWM = BM / WM;
@@ -129,7 +145,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   constexpr int XB = BM / (8 * NW);
   constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
-  static_assert(NSW >= 2 && NSW <= 3 && NSX >= 2 && NSX <= 3, "stages");
+  static_assert(NSW >= 2 && NSW <= 4 && NSX >= 2 && NSX <= 3, "stages");
 
   // With a K split, entries [q*count, (q+1)*count) run K range q of every
   // tile and write their partial sums to output q.
@@ -149,10 +165,18 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 
   // NSW weight and NSX token stage buffers, as separate arrays so the
   // compiler can tell reads of one buffer from DMA still landing in another
-  // (an unused third one is a token 16 bytes).
+  // (with one array per operand it waits for every copy before each read).
+  // Stages past NSW / NSX point at a used buffer, chosen at compile time, so
+  // their arrays are never referenced and take no LDS.
   constexpr int SW = WROWS * BK, SX = BM * BK;
-  __shared__ __attribute__((aligned(1024))) uint16_t lw0[SW], lw1[SW], lw2[NSW > 2 ? SW : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lx0[SX], lx1[SX], lx2[NSX > 2 ? SX : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lw0[SW], lw1[SW];
+  __shared__ __attribute__((aligned(1024))) uint16_t lw2_[NSW > 2 ? SW : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lw3_[NSW > 3 ? SW : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lx0[SX], lx1[SX];
+  __shared__ __attribute__((aligned(1024))) uint16_t lx2_[NSX > 2 ? SX : 8];
+  uint16_t* const lw2 = NSW > 2 ? lw2_ : lw0;
+  uint16_t* const lw3 = NSW > 3 ? lw3_ : lw0;
+  uint16_t* const lx2 = NSX > 2 ? lx2_ : lx0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -191,7 +215,8 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   // add nothing.  (A separate code path for a partial turn made the compiler
   // add a full drain at the top of its loop.)  The other rings run the
   // slabs left over after whole turns as straight-line code.
-  constexpr int P = NSW == NSX ? NSW : NSW * NSX;
+  constexpr int P = NSW == NSX ? NSW : NSW % NSX == 0 ? NSW : NSW * NSX;  // lcm for 2..4
+  static_assert(P == 2 || P == 3 || P == 4 || P == 6, "ring turn");
   constexpr bool kPadTurns = NSW == 3 && NSX == 3;
   const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
   const int pad = kPadTurns ? (P - nk % P) % P : 0;
@@ -199,13 +224,21 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   auto dma_w = [&](int kt_local, uint16_t* lw) {
     const int s = kt_local - pad;
     const uint32_t koff = s < 0 ? 0u : (uint32_t)(kb + s) * (BK * 2);
-    dma_tile<WOFF, NW, kPolW>(s < 0 ? rzero : rw0, koff, woff, lw, wave);
-    if (UPGATE) dma_tile<WOFF, NW, kPolW>(s < 0 ? rzero : rw1, koff, woff, lw + BN * BK, wave);
+    dma_tile<WOFF, NW, POLW>(s < 0 ? rzero : rw0, koff, woff, lw, wave);
+    if (UPGATE) dma_tile<WOFF, NW, POLW>(s < 0 ? rzero : rw1, koff, woff, lw + BN * BK, wave);
   };
+  // Token copy blocks whose 8 rows all lie past the tile's last row (a
+  // group's short last tile) read through the size-0 descriptor: zeros, no
+  // memory traffic, and the same instruction count, so every vmcnt wait
+  // below still counts the same copies.  The rows they fill are never stored.
+  uint32_t xlive = 0;
+#pragma unroll
+  for (int i = 0; i < XB; ++i)
+    if (tl.m0 + 8 * (wave + NW * i) < tl.m_end) xlive |= 1u << i;
   auto dma_x = [&](int kt_local, uint16_t* lx) {
     const int s = kt_local - pad;
     const uint32_t koff = s < 0 ? 0u : (uint32_t)(kb + s) * (BK * 2);
-    dma_tile<XB, NW, kPolX>(s < 0 ? rzero : rx, koff, xoff, lx, wave);
+    dma_tile_live<XB, NW, kPolX>(s < 0 ? rzero : rx, rzero, xlive, koff, xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -276,7 +309,12 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   // may stay in flight.
   static_assert(NSX <= NSW, "the token ring is never the longer one");
   constexpr int NWI = (UPGATE ? 2 : 1) * WOFF;  // weight copies per slab
-  constexpr int WAIT = NSX == NSW ? (NSW - 2) * NDMA : NWI + (NSW - NSX - 1) * NDMA;
+  // Copies issued after the last one slab J + 1 needs: with equal rings the
+  // weights of J + 1 (issued in slab J + 2 - NSW, last in that slab), then
+  // NSW - 2 whole slabs; with a longer weight ring the tokens of J + 1
+  // (issued in slab J + 2 - NSX, before that slab's weight copies), then
+  // NSX - 2 whole slabs.
+  constexpr int WAIT = NSX == NSW ? (NSW - 2) * NDMA : NWI + (NSX - 2) * NDMA;
   static_assert(WAIT <= 63, "vmcnt range");
   auto dma = [&](int kt_w, uint16_t* lw, int kt_x, uint16_t* lx) {
     if constexpr (NSX < NSW) {
@@ -298,13 +336,17 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   const int m = nk + pad;  // slabs to run
   // Ring buffer i of each operand (i a constant, so the named array is used
   // directly and the compiler keeps telling the stages apart).
-#define MOE_WB(i) ((i) == 0 ? lw0 : (i) == 1 ? lw1 : lw2)
+#define MOE_WB(i) ((i) == 0 ? lw0 : (i) == 1 ? lw1 : (i) == 2 ? lw2 : lw3)
 #define MOE_XB(i) ((i) == 0 ? lx0 : (i) == 1 ? lx1 : lx2)
   if (m > 0) {
-    // Copies of the slabs before 0, in the order a slab issues them.
-    // (Slab -2 exists only for a 3-stage weight ring; slab -1 copies the
-    // tokens of slab 0 or 1 and the weights of slab 0 or 1.)
-    if constexpr (NSW == 3 && NSX == 2) {
+    // Copies of the slabs before 0, in the order a slab issues them: slab
+    // q < 0 copies the tokens of q + NSX - 1 and the weights of q + NSW - 1
+    // where those are >= 0.
+    if constexpr (NSW == 4 && NSX == 2) {
+      dma_w(0, lw0);
+      dma_w(min(1, m - 1), lw1);
+      dma(min(2, m - 1), lw2, 0, lx0);
+    } else if constexpr (NSW == 3 && NSX == 2) {
       dma_w(0, lw0);
       dma(min(1, m - 1), lw1, 0, lx0);
     } else if constexpr (NSW == 3) {
@@ -348,6 +390,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
       MOE_SLAB(j, 0)                                    \
       MOE_SLAB(j + 1, 1)                                \
       if constexpr (P >= 3) MOE_SLAB(j + 2, 2)          \
+      if constexpr (P == 4) MOE_SLAB(j + 3, 3)          \
       if constexpr (P == 6) {                           \
         MOE_SLAB(j + 3, 3)                              \
         MOE_SLAB(j + 4, 4)                              \
@@ -1083,10 +1126,14 @@ constexpr int kWStages256 = 3, kXStages256 = 2, kWStages128 = 3, kXStages128 = 3
 constexpr int kUp256WM = 128, kUp256WN = 64, kDown256WM = 128, kDown256WN = 128;
 
 template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX>
-static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
+static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a, bool stream_w) {
   constexpr int nw = (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX>), grid, dim3(64 * nw), 0,
-                     s, a);
+  if (stream_w)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX, kWeightPolicy>), grid,
+                       dim3(64 * nw), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX, 0>), grid,
+                       dim3(64 * nw), 0, s, a);
 }
 
 hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
@@ -1112,9 +1159,11 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   else if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, 2>), grid, block, 0, s, up_args(P, x));
   else if (P.up.bm == 128)
-    launch_gemm<128, 128, 128, 32, true, kWStages128, kXStages128>(grid, s, up_args(P, x));
+    launch_gemm<128, 128, 128, 32, true, kWStages128, kXStages128>(grid, s, up_args(P, x),
+                                                                   P.up.stream_w);
   else
-    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x));
+    launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x),
+                                                                             false);
   return hipGetLastError();
 }
 
@@ -1141,10 +1190,11 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
   else if (P.kind == KIND_BF16_DECODE)
     hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, 2>), grid, block, 0, s, down_args(P, x));
   else if (P.down.bm == 128)
-    launch_gemm<128, 256, 128, 64, false, kWStages128, kXStages128>(grid, s, down_args(P, x));
+    launch_gemm<128, 256, 128, 64, false, kWStages128, kXStages128>(grid, s, down_args(P, x),
+                                                                    P.down.stream_w);
   else
-    launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(grid, s,
-                                                                                  down_args(P, x));
+    launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(
+        grid, s, down_args(P, x), false);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ struct GemmShape {
   int n_fastest;          // within a schedule chunk: 0 = row tile fastest, 1 = column
   int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
   int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
+  int stream_w;           // weight bursts non-temporal (prefill kernels, 128-row tiles)
 };
 
 struct Plan {
