@@ -100,7 +100,7 @@ int forward_impl(const moe_desc* d, const void* x, const void* w_router,
                   (const uint8_t*)mx->down, (const uint8_t*)mx->s_up,
                   (const uint8_t*)mx->s_gate, (const uint8_t*)mx->s_down};
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted, tu, td,
-               W.at<void>(P.o_h), out, P.down.ksplit, sc};
+               W.at<void>(P.o_h), out, P.down.ksplit, sc, W.at<float>(P.o_part)};
   const int64_t part_stride = ((int64_t)P.R + kRowSlack) * d->d;
   // With a split router and one token block (at most 16 tokens) the router
   // also runs the dispatch, and events 1 and 2 mark the same point.
@@ -265,7 +265,7 @@ int moe_experts(const moe_desc* d, const void* x, const void* w_up, const void* 
   Tile* td = W.at<Tile>(P.o_tiles_down);
   MOE_TRY(launch_tiles(P, group_offsets, tu, td, s));
   ExpertArgs a{x, w_up, w_gate, w_down, ws_up, ws_gate, ws_down, sorted_token, tu, td,
-               W.at<void>(P.o_h), expert_out, 1};
+               W.at<void>(P.o_h), expert_out, 1, MxScales{}, W.at<float>(P.o_part)};
   MOE_TRY(launch_expert_up(P, a, s));
   MOE_TRY(launch_expert_down(P, a, s));
   return MOE_OK;

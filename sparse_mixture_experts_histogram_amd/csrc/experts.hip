@@ -50,7 +50,34 @@ struct GemmArgs {
   // MX-format experts: w0/w1/s0/s1 hold E2M1 codes [., N, K/2] (MXFP4) or
   // E4M3 codes [., N, K] (MXFP8) and these their E8M0 scales [., N, K/32]
   const uint8_t *sw0, *sw1, *ss0, *ss1;
+  // Last-round split (prefill kernels): with sk_cus > 0 the tiles of a last,
+  // partly filled round of sk_cus workgroups are cut along K into pieces
+  // whose float32 accumulators go to `part` and are added by the fixup
+  // kernel (see sk_layout).
+  float* part;
+  int sk_cus;
 };
+
+// Schedule of the last-round split.  `count` tiles on C workgroup slots run
+// count / C whole rounds and r = count % C tiles in a last round that leaves
+// C - r slots idle.  Those r tiles are cut into s = C / r pieces along K (at
+// least kSkMinSlabs slabs each), so the last round runs r * s pieces of
+// about 1 / s of a tile.  Entries [0, dp) are whole tiles; entry dp + t * s +
+// j is piece j of tile dp + t.  No split (r = 0, s = 1) when the last round
+// is full or a piece would be too short.
+constexpr int kSkMinSlabs = 8;
+struct SkLayout {
+  int dp, r, s;
+};
+__device__ __forceinline__ SkLayout sk_layout(int count, int C, int nk) {
+  SkLayout L{count, 0, 1};
+  if (C <= 0) return L;
+  const int r = count % C;
+  if (r == 0) return L;
+  const int s = min(C / r, nk / kSkMinSlabs);
+  if (s < 2) return L;
+  return SkLayout{count - r, r, s};
+}
 
 constexpr int BK = 64;  // K slab: 8 chunks of 8 bf16 per tile row (one 128-byte line)
 
@@ -129,6 +156,109 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
+// Float32 accumulators of one wave in register order: accumulator c of the
+// wave at ((wave * NACC + c) * 64 + lane) * 16 floats (16-byte accesses,
+// consecutive lanes contiguous).
+template <int NS, int TN, int TM>
+__device__ __forceinline__ void store_partial(f32x16 (&acc)[NS][TN][TM], float* dst, int wave,
+                                              int lane) {
+  constexpr int NACC = NS * TN * TM;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        float4* d = (float4*)(dst + ((wave * NACC + (s * TN + i) * TM + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          d[q] = make_float4(acc[s][i][j][4 * q], acc[s][i][j][4 * q + 1], acc[s][i][j][4 * q + 2],
+                             acc[s][i][j][4 * q + 3]);
+      }
+}
+// acc (+)= one stored partial (LOAD: acc = partial; else acc += partial).
+template <int NS, int TN, int TM, bool LOAD>
+__device__ __forceinline__ void add_partial(f32x16 (&acc)[NS][TN][TM], const float* src, int wave,
+                                            int lane) {
+  constexpr int NACC = NS * TN * TM;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const float4* p =
+            (const float4*)(src + ((wave * NACC + (s * TN + i) * TM + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 u = p[q];
+          if (LOAD) {
+            acc[s][i][j][4 * q] = u.x;
+            acc[s][i][j][4 * q + 1] = u.y;
+            acc[s][i][j][4 * q + 2] = u.z;
+            acc[s][i][j][4 * q + 3] = u.w;
+          } else {
+            acc[s][i][j][4 * q] += u.x;
+            acc[s][i][j][4 * q + 1] += u.y;
+            acc[s][i][j][4 * q + 2] += u.z;
+            acc[s][i][j][4 * q + 3] += u.w;
+          }
+        }
+      }
+}
+
+// D[n = feature][m = row]: lane holds row (lane & 31) and, for q = 0..3,
+// features 8q + 4*(lane>>5) + 0..3 of each 32x32 sub-tile.  Outputs are
+// written through LDS so that every store is a 16-byte piece of a whole
+// row: each wave stages 32 rows x WN features of its tile at a time in a
+// stage buffer of its own (row pitch padded by 16 bytes against bank
+// conflicts), then stores them as 16-byte pieces, consecutive lanes along
+// a row.
+template <int WM, int WN, int TN, int TM, bool UPGATE>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[UPGATE ? 2 : 1][TN][TM], const Tile& tl,
+                                              int N, const GemmArgs& a, int split, char* st,
+                                              int wm, int wn, int lane) {
+  constexpr int ES = UPGATE ? 2 : 4;                  // output element bytes
+  constexpr int RB = WN * ES, PITCH = RB + 16;        // staged row bytes, LDS pitch
+  constexpr int LPR = RB / 16;                         // 16-byte pieces per staged row
+  static_assert(RB % 16 == 0, "epilogue shape");
+  const int row0 = tl.m0 + wm * WM, col0 = tl.n0 + wn * WN;
+  char* outb = (char*)a.out + (int64_t)split * a.split_stride * ES;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        char* dst = st + (lane & 31) * PITCH + (i * 32 + 8 * q + 4 * (lane >> 5)) * ES;
+        if (UPGATE) {
+          uint16_t hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            hv[r] = f32_to_bf16(silu_mul(acc[1][i][j][4 * q + r], acc[0][i][j][4 * q + r]));
+          uint2 pk;
+          pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+          pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+          *(uint2*)dst = pk;
+        } else {
+          *(float4*)dst = make_float4(acc[0][i][j][4 * q + 0], acc[0][i][j][4 * q + 1],
+                                      acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int id0 = 0; id0 < 32 * LPR; id0 += 64) {
+      const int id = id0 + lane, r = id / LPR, cb = (id % LPR) * 16;
+      if (id < 32 * LPR) {
+        const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
+        const int row = row0 + j * 32 + r, col = col0 + cb / ES;
+        if (row < tl.m_end && col < N)
+          *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
+      }
+    }
+  }
+}
+
 constexpr int kPolX = 0;  // cache policy bits of the token bursts
 constexpr int kSpread = 2;            // k-steps of a slab over which its DMAs are issued
 // POLW: cache policy bits of the weight bursts (0, or non-temporal when each
@@ -148,11 +278,30 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   static_assert(NSW >= 2 && NSW <= 4 && NSX >= 2 && NSX <= 3, "stages");
 
   // With a K split, entries [q*count, (q+1)*count) run K range q of every
-  // tile and write their partial sums to output q.
+  // tile and write their partial sums to output q.  With the last-round
+  // split (never together with a K split) an entry past the whole tiles is
+  // one K piece of a last-round tile, whose accumulators go to a.part.
+  // The whole tiles take the first dpb workgroups (remapped per XCD); the
+  // pieces take one workgroup each after them, in order, so consecutive
+  // pieces land on different XCDs and are dispatched last.  (Remapping
+  // them with the whole tiles gave some XCDs only whole tiles.)
   const int count = a.tiles[0].g;
-  const int idx = entry_of_block(count * a.ksplit, a.xcd_remap);
-  if (idx < 0) return;
-  const int split = idx / count, L = idx - split * count;
+  const SkLayout sk = sk_layout(count, a.sk_cus, min(a.K_r, a.K_s) / BK);
+  const int dpb = ((sk.dp * a.ksplit + 7) >> 3) << 3;
+  int split, nsplit, L, piece = -1;
+  if ((int)blockIdx.x >= dpb) {
+    piece = blockIdx.x - dpb;
+    if (piece >= sk.r * sk.s) return;
+    L = sk.dp + piece / sk.s;
+    split = piece % sk.s;
+    nsplit = sk.s;
+  } else {
+    const int idx = entry_of_block(sk.dp * a.ksplit, a.xcd_remap);
+    if (idx < 0) return;
+    split = idx / count;
+    L = idx - split * count;
+    nsplit = a.ksplit;
+  }
   const Tile tl = uniform_tile(a.tiles[1 + L]);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
@@ -204,7 +353,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
     xoff[i] = (src_row * (uint32_t)a.ldt + gch * 8) * 2;
   }
   const int nk_all = K / BK;
-  const int kb = split * nk_all / a.ksplit;  // first slab of this K range
+  const int kb = split * nk_all / nsplit;  // first slab of this K range
   const uint32_t wbytes = (uint32_t)(wstride * 2);
   const __amdgpu_buffer_rsrc_t rw0 = buffer_of(W0, wbytes);
   const __amdgpu_buffer_rsrc_t rw1 = buffer_of(UPGATE ? W1 : W0, wbytes);
@@ -218,7 +367,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   constexpr int P = NSW == NSX ? NSW : NSW % NSX == 0 ? NSW : NSW * NSX;  // lcm for 2..4
   static_assert(P == 2 || P == 3 || P == 4 || P == 6, "ring turn");
   constexpr bool kPadTurns = NSW == 3 && NSX == 3;
-  const int nk = (split + 1) * nk_all / a.ksplit - kb;  // slabs of this K range
+  const int nk = (split + 1) * nk_all / nsplit - kb;  // slabs of this K range
   const int pad = kPadTurns ? (P - nk % P) % P : 0;
   const __amdgpu_buffer_rsrc_t rzero = buffer_of(W0, 0);
   auto dma_w = [&](int kt_local, uint16_t* lw) {
@@ -448,55 +597,43 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
   }
 
-  // D[n = feature][m = row]: lane holds row (lane & 31) and, for q = 0..3,
-  // features 8q + 4*(lane>>5) + 0..3 of each 32x32 sub-tile.  Outputs are
-  // written through LDS so that every store is a 16-byte piece of a whole
-  // row: each wave stages 32 rows x WN features of its tile at a time in a
-  // stage buffer of its own (row pitch padded by 16 bytes against bank
-  // conflicts), then stores them as 16-byte pieces, consecutive lanes along
-  // a row.
-  constexpr int ES = UPGATE ? 2 : 4;                  // output element bytes
-  constexpr int RB = WN * ES, PITCH = RB + 16;        // staged row bytes, LDS pitch
-  constexpr int LPR = RB / 16;                         // 16-byte pieces per staged row
-  static_assert(NW == 4 && RB % 16 == 0, "epilogue shape");
+  if (piece >= 0) {  // a K piece of a last-round tile: accumulators to a.part
+    store_partial<NS, TN, TM>(acc, a.part + (size_t)piece * (NW * NS * TN * TM * 1024), wave,
+                              lane);
+    return;
+  }
+  constexpr int PITCH = WN * (UPGATE ? 2 : 4) + 16;
+  static_assert(NW == 4, "epilogue shape");
   static_assert(32 * PITCH <= 2 * (SX < SW ? SX : SW), "staging fits a stage buffer");
   __syncthreads();  // every wave is done reading the stage buffers
   char* st = (char*)(wave == 0 ? lw0 : wave == 1 ? lw1 : wave == 2 ? lx0 : lx1);
-  const int row0 = tl.m0 + wm * WM, col0 = tl.n0 + wn * WN;
-  char* outb = (char*)a.out + (int64_t)split * a.split_stride * ES;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        char* dst = st + (lane & 31) * PITCH + (i * 32 + 8 * q + 4 * (lane >> 5)) * ES;
-        if (UPGATE) {
-          uint16_t hv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            hv[r] = f32_to_bf16(silu_mul(acc[1][i][j][4 * q + r], acc[0][i][j][4 * q + r]));
-          uint2 pk;
-          pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-          pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *(uint2*)dst = pk;
-        } else {
-          *(float4*)dst = make_float4(acc[0][i][j][4 * q + 0], acc[0][i][j][4 * q + 1],
-                                      acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3]);
-        }
-      }
-    }
-#pragma unroll
-    for (int id0 = 0; id0 < 32 * LPR; id0 += 64) {
-      const int id = id0 + lane, r = id / LPR, cb = (id % LPR) * 16;
-      if (id < 32 * LPR) {
-        const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
-        const int row = row0 + j * 32 + r, col = col0 + cb / ES;
-        if (row < tl.m_end && col < N)
-          *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
-      }
-    }
-  }
+  tile_epilogue<WM, WN, TN, TM, UPGATE>(acc, tl, N, a, split, st, wm, wn, lane);
+}
+
+// Adds the K pieces of each last-round tile of a split GEMM launch (see
+// sk_layout), in piece order, and writes the tile as the GEMM epilogue does
+// (SwiGLU and bf16 h for up/gate, float32 for down).  Workgroup t handles
+// split tile dp + t; the piece accumulators use the GEMM's register layout.
+template <int BM, int BN, int WM, int WN, bool UPGATE>
+__global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fixup_kernel(GemmArgs a) {
+  constexpr int NWN = BN / WN, NWM = BM / WM, NW = NWN * NWM;
+  constexpr int TN = WN / 32, TM = WM / 32, NS = UPGATE ? 2 : 1;
+  constexpr int PITCH = WN * (UPGATE ? 2 : 4) + 16;
+  constexpr size_t PIECE = (size_t)NW * NS * TN * TM * 1024;  // floats per piece
+  __shared__ __attribute__((aligned(16))) char stage[NW][32 * PITCH];
+  const SkLayout sk = sk_layout(a.tiles[0].g, a.sk_cus, min(a.K_r, a.K_s) / BK);
+  const int t = blockIdx.x;
+  if (t >= sk.r) return;
+  const Tile tl = uniform_tile(a.tiles[1 + sk.dp + t]);
+  const int N = tl.g >= a.E ? a.N_s : a.N_r;
+  if (tl.n0 >= N) return;  // the GEMM wrote no pieces for it either
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x16 acc[NS][TN][TM];
+  const float* base = a.part + (size_t)t * sk.s * PIECE;
+  add_partial<NS, TN, TM, true>(acc, base, wave, lane);
+  for (int j = 1; j < sk.s; ++j) add_partial<NS, TN, TM, false>(acc, base + j * PIECE, wave, lane);
+  tile_epilogue<WM, WN, TN, TM, UPGATE>(acc, tl, N, a, 0, stage[wave], wave / NWN, wave % NWN,
+                                        lane);
 }
 
 // ---------------------------------------------------------------- decode
@@ -1102,7 +1239,7 @@ static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
                   (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
                   (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
                   x.tiles_up, P.up.xcd_remap, 1, 0, (uint32_t)(D.T * D.d * 2),
-                  x.mx.up, x.mx.gate, x.mx.s_up, x.mx.s_gate};
+                  x.mx.up, x.mx.gate, x.mx.s_up, x.mx.s_gate, x.part, P.up.sk_cus};
 }
 static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
@@ -1112,7 +1249,7 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
                   x.tiles_down, P.down.xcd_remap, x.ksplit,
                   (int64_t)((size_t)P.R + kRowSlack) * D.d,
                   (uint32_t)(((size_t)P.R + kRowSlack) * P.ffn_max * 2), x.mx.down, nullptr,
-                  x.mx.s_down, nullptr};
+                  x.mx.s_down, nullptr, x.part, P.down.sk_cus};
 }
 
 // LDS stages (weights, tokens) of the prefill GEMM instantiations, at most
@@ -1128,6 +1265,13 @@ constexpr int kUp256WM = 128, kUp256WN = 64, kDown256WM = 128, kDown256WN = 128;
 template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX>
 static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a, bool stream_w) {
   constexpr int nw = (BM / WM) * (BN / WN);
+  if (a.sk_cus > 0) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX, 0>),
+                       dim3(grid.x + 8 + (unsigned)a.sk_cus), dim3(64 * nw), 0, s, a);
+    hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, UPGATE>), dim3((unsigned)a.sk_cus),
+                       dim3(64 * nw), 0, s, a);
+    return;
+  }
   if (stream_w)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX, kWeightPolicy>), grid,
                        dim3(64 * nw), 0, s, a);

@@ -54,6 +54,7 @@ struct ExpertArgs {
                   // (R + kRowSlack) rows each, summed by the combine
   int ksplit;     // K ranges of the down GEMM (1 = direct result)
   MxScales mx;    // MX-format expert weights: their scales
+  float* part;    // K-piece accumulators of a last-round split (see plan.h GemmShape::sk_cus)
 };
 
 // Grouped up/gate GEMM + SwiGLU (writes h).

@@ -166,14 +166,30 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.up.xcd_remap = 1;
   P.down.n_fastest = 1;
   P.down.xcd_remap = 1;
-  // A down GEMM with under three tiles per CU loses much of its last round to
-  // idle CUs; when its K is long (>= 8192) splitting K in two doubles the
-  // tiles at little per-tile cost (the combine adds the two partial outputs in
-  // a fixed order).  Measured: Mixtral-shaped T=4096 down 1.13 -> 1.08 ms;
-  // short-K layers got slower, so they keep one range.
+  // A down GEMM of 128-row tiles with under three tiles per CU loses much of
+  // its last round to idle CUs; when its K is long (>= 8192) splitting K in
+  // two doubles the tiles at little per-tile cost (the combine adds the two
+  // partial outputs in a fixed order).  Measured (on 256-row tiles, before
+  // the last-round split below replaced it there): Mixtral-shaped T=4096
+  // down 1.13 -> 1.08 ms; short-K layers got slower, so they keep one range.
   P.up.ksplit = 1;
   P.down.ksplit = 1;
-  if (P.kind == KIND_BF16_PREFILL) {
+  // A down GEMM of 256-row tiles with a long K (>= 8192) splits the tiles
+  // of its last, partly filled round along K into pieces added by a fixup
+  // kernel (sk_layout in experts.hip).  Measured on MI355X, Mixtral-shaped
+  // T=4096: 560 whole tiles of 224 slabs (371 us each) in two full rounds,
+  // then 48 tiles as 240 pieces of 45 slabs (88 us each); down GEMM plus
+  // combine 0.961 -> 0.915 ms against the two-way K split of every tile
+  // (whose combine added two partial buffers).  Each piece carries about
+  // 20 us of fixed cost (prologue, a 256 KB float32 partial write and its
+  // fixup read), so shorter reductions lost: the mid-size layer's 32- and
+  // 16-slab tiles ran 14% and 29% slower split, and the up/gate GEMM gained
+  // nothing.
+  P.up.sk_cus = P.down.sk_cus = 0;
+  const int k_down_max = std::max(d->ffn, d->n_shared ? d->ffn_shared : 0);
+  if (P.kind == KIND_BF16_PREFILL && P.down.bm == 256 && k_down_max >= 8192)
+    P.down.sk_cus = kCUs;
+  if (P.kind == KIND_BF16_PREFILL && !P.down.sk_cus) {
     const int64_t est_tiles =
         (cdiv(P.pairs, P.down.bm) + std::min<int64_t>(d->E, P.pairs) / 2) * P.down.n_tiles;
     const int k_down = std::max(d->ffn, d->n_shared ? d->ffn_shared : 0);
@@ -216,6 +232,13 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.o_w = take((size_t)P.pairs * 4);
   P.o_h = take(rows_ws * (size_t)P.ffn_max * eb);
   P.o_out = take(rows_ws * (size_t)d->d * 4 * P.down.ksplit);
+  // K-piece accumulators: at most kCUs pieces of one tile (BM x weight rows
+  // of up/gate, BM x BN of down) in float32
+  const size_t piece_up = (size_t)P.up.bm * 2 * P.up.bn * 4;
+  const size_t piece_dn = (size_t)P.down.bm * P.down.bn * 4;
+  P.o_part = take(P.up.sk_cus || P.down.sk_cus
+                      ? (size_t)kCUs * std::max(P.up.sk_cus ? piece_up : 0, P.down.sk_cus ? piece_dn : 0)
+                      : 0);
   P.total = o;
   *p = P;
   return MOE_OK;

@@ -22,6 +22,9 @@ constexpr int64_t kRouterWideMinWeights = 1 << 19;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
+// Compute units of an MI355X (gfx950): the workgroup slots of one round of
+// one-workgroup-per-CU GEMM tiles.
+constexpr int kCUs = 256;
 // Rows of slack after the grouped rows so tile loads past the end stay in bounds.
 constexpr int kRowSlack = 256;
 // Router option bits: sigmoid scores with a selection-only bias; raw weights.
@@ -55,6 +58,7 @@ struct GemmShape {
   int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
   int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
   int stream_w;           // weight bursts non-temporal (prefill kernels, 128-row tiles)
+  int sk_cus;             // last-round split over this many workgroup slots (0: off)
 };
 
 struct Plan {
@@ -73,7 +77,7 @@ struct Plan {
   GemmShape up, down;
   // workspace byte offsets
   size_t o_router_part, o_blk_hist, o_blk_rank, o_counts, o_offsets, o_tiles_up, o_tiles_down, o_sorted,
-      o_slot, o_idx, o_w, o_h, o_out, total;
+      o_slot, o_idx, o_w, o_h, o_out, o_part, total;
 };
 
 enum KernelKind {

@@ -53,6 +53,14 @@ SMALL = {c.name: c for c in [
     # one with 2) and a shared expert of 1200 rows
     custom("split_tiles", 117, T=1200, d=256, E=16, k=2, ffn=192, n_shared=1, ffn_shared=320,
            bias="normal", bias_var=0.5),
+    # a down GEMM of 256-row tiles with K >= 8192 whose last round is split
+    # along K into pieces added by the fixup kernel (4 tiles on 256 slots:
+    # 16 pieces of 8 slabs each)
+    custom("last_round", 118, T=800, d=256, E=2, k=1, ffn=8192),
+    # the same with a shared expert whose reduction is longer than the
+    # routed experts' (pieces of unequal length), 16 tiles of 16 pieces
+    custom("last_round_shared", 119, T=800, d=512, E=2, k=1, ffn=8192, n_shared=1,
+           ffn_shared=8448, bias="normal", bias_var=0.5),
     NAMED["tiny_f32"],
 ]}
 
