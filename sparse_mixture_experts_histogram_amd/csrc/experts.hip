@@ -260,7 +260,6 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[UPGATE ? 2 : 1][TN][
 }
 
 constexpr int kPolX = 0;  // cache policy bits of the token bursts
-constexpr int kSpread = 2;            // k-steps of a slab over which its DMAs are issued
 // POLW: cache policy bits of the weight bursts (0, or non-temporal when each
 // weight tile is read by a single row tile).
 template <int BM, int BN, int WM, int WN, bool UPGATE, int NSW, int NSX, int POLW>
@@ -428,7 +427,10 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   };
   constexpr int NF = TM + NS * TN;   // fragment reads per k-step
   constexpr int NMF = NS * TN * TM;  // MFMAs per k-step
-  // DMAs issued during k-steps 0, 1 and 2 of a slab
+  // DMAs issued during k-steps 0, 1 and 2 of a slab: over kSpread k-steps,
+  // at most one per MFMA of a k-step
+  constexpr int kSpread = (NDMA + NMF - 1) / NMF < 2 ? 2 : (NDMA + NMF - 1) / NMF;
+  static_assert(kSpread <= 3, "DMAs fit three k-steps");
   constexpr int ND0 = (NDMA + kSpread - 1) / kSpread;
   constexpr int ND1 = kSpread >= 2 ? (NDMA - ND0 + kSpread - 2) / (kSpread - 1) : 0;
   constexpr int ND2 = NDMA - ND0 - ND1;
@@ -603,10 +605,16 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
     return;
   }
   constexpr int PITCH = WN * (UPGATE ? 2 : 4) + 16;
+  constexpr int STG = 32 * PITCH;  // staging bytes per wave
   static_assert(NW == 4, "epilogue shape");
-  static_assert(32 * PITCH <= 2 * (SX < SW ? SX : SW), "staging fits a stage buffer");
   __syncthreads();  // every wave is done reading the stage buffers
-  char* st = (char*)(wave == 0 ? lw0 : wave == 1 ? lw1 : wave == 2 ? lx0 : lx1);
+  char* st;
+  if constexpr (STG <= 2 * (SX < SW ? SX : SW)) {  // one stage buffer per wave
+    st = (char*)(wave == 0 ? lw0 : wave == 1 ? lw1 : wave == 2 ? lx0 : lx1);
+  } else {  // small token stages: two waves per weight stage
+    static_assert(2 * STG <= 2 * SW, "staging fits the weight stages");
+    st = (char*)(wave & 1 ? lw1 : lw0) + (wave >> 1) * STG;
+  }
   tile_epilogue<WM, WN, TN, TM, UPGATE>(acc, tl, N, a, split, st, wm, wn, lane);
 }
 
@@ -1254,7 +1262,8 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
 
 // LDS stages (weights, tokens) of the prefill GEMM instantiations, at most
 // 160 KB: 256-row tiles hold 3 x 32 KB of weight slabs and 2 x 32 KB of
-// token slabs, 128-row tiles 3 x (32 + 16) KB.  Measured on MI355X against
+// token slabs, 128-row tiles 3 x (32 + 16) KB, 64-row tiles 2 x (32 + 8) KB
+// (two workgroups per CU).  Measured on MI355X against
 // 2 + 2 stages for 256-row tiles: Mixtral-shaped T=4096 layer 2.93 -> 2.62
 // ms; a 16-slab down GEMM 0.116 -> 0.109 ms.
 constexpr int kWStages256 = 3, kXStages256 = 2, kWStages128 = 3, kXStages128 = 3;
@@ -1305,6 +1314,8 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
   else if (P.up.bm == 128)
     launch_gemm<128, 128, 128, 32, true, kWStages128, kXStages128>(grid, s, up_args(P, x),
                                                                    P.up.stream_w);
+  else if (P.up.bm == 64)
+    launch_gemm<64, 128, 64, 32, true, 2, 2>(grid, s, up_args(P, x), P.up.stream_w);
   else
     launch_gemm<256, 128, kUp256WM, kUp256WN, true, kWStages256, kXStages256>(grid, s, up_args(P, x),
                                                                              false);
@@ -1336,6 +1347,8 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
   else if (P.down.bm == 128)
     launch_gemm<128, 256, 128, 64, false, kWStages128, kXStages128>(grid, s, down_args(P, x),
                                                                     P.down.stream_w);
+  else if (P.down.bm == 64)
+    launch_gemm<64, 256, 64, 64, false, 2, 2>(grid, s, down_args(P, x), P.down.stream_w);
   else
     launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(
         grid, s, down_args(P, x), false);

@@ -10,9 +10,15 @@ namespace moe {
 // Tile shapes (rows per tile, output columns per tile) of the two grouped
 // GEMMs for each kernel family; they must match the kernel instantiations
 // launched in experts.hip.  Prefill uses 256-row tiles when experts average
-// at least 384 rows (less padding is then worth the larger reuse), else 128.
+// at least 384 rows (less padding is then worth the larger reuse), 64-row
+// tiles when they average at most 32 (80 KB of LDS, two workgroups per CU,
+// so twice the copies in flight for these weight-streaming layers; measured
+// on MI355X: gpt-oss-shaped T=512, 16 rows per expert, 1.125 -> 1.093 ms;
+// the DeepSeek-V3-shaped layer, 128 rows per expert, was 9% slower on them),
+// else 128.
 static int prefill_rows(const moe_desc* d) {
-  return d->T * d->k >= 384LL * d->E ? 256 : 128;
+  const int64_t pairs = d->T * d->k;
+  return pairs >= 384LL * d->E ? 256 : pairs <= 32LL * d->E ? 64 : 128;
 }
 // The streaming kernels use 16-row tiles of 16 (bf16) or 32 (MXFP4) columns;
 // MXFP4 layers with at least one (token, expert) pair per expert and a
@@ -195,14 +201,14 @@ int make_plan(const moe_desc* d, Plan* p) {
     const int k_down = std::max(d->ffn, d->n_shared ? d->ffn_shared : 0);
     if (est_tiles < 3 * 256 && k_down >= 8192) P.down.ksplit = 2;
   }
-  // Weight bursts of the 128-row prefill tiles skip the caches' normal
-  // retention when experts average at most a quarter tile of rows: nearly
-  // every weight tile is then read by one row tile only.  Measured on MI355X:
+  // Weight bursts of the 64- and 128-row prefill tiles skip the caches'
+  // normal retention when experts average at most a quarter tile of rows:
+  // nearly every weight tile is then read by one row tile only.  Measured on MI355X:
   // gpt-oss-shaped layer at T=512 (16 rows per expert) 1.175 -> 1.121 ms;
   // with many rows per expert (several row tiles re-reading each weight
   // tile, DeepSeek-V3-shaped T=4096) the same policy was 6% slower.
   P.up.stream_w = P.down.stream_w = 0;
-  if (P.kind == KIND_BF16_PREFILL && P.up.bm == 128 && P.pairs * 4 <= 128LL * d->E)
+  if (P.kind == KIND_BF16_PREFILL && P.up.bm <= 128 && P.pairs * 4 <= (int64_t)P.up.bm * d->E)
     P.up.stream_w = P.down.stream_w = 1;
   // A split down GEMM measured faster with its entries spread over all XCDs.
   if (P.down.ksplit > 1) P.down.xcd_remap = 0;
