@@ -52,6 +52,8 @@ WORKLOADS = {
     "gpt_oss_t128": ("gpt_oss", 128, "flushed"),
     "gpt_oss_t512": ("gpt_oss", 512, "flushed"),
 }
+# The gpt-oss-shaped layer with MX-format experts (profiling runs only).
+MX_WORKLOADS = {"mxfp4_gpt_oss_decode": "mxfp4", "mxfp8_gpt_oss_decode": "mxfp8"}
 
 
 def parse():
@@ -72,7 +74,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle runs (median taken)")
     ap.add_argument("--workload", default="all",
                     help="'all' (default: the headline plus every config), or one of "
-                         + ", ".join(WORKLOADS) + " to time that layer alone (for profiling)")
+                         + ", ".join(WORKLOADS) + " to time that layer alone (for profiling), "
+                         "or " + " / ".join(MX_WORKLOADS) + " for the gpt-oss-shaped layer "
+                         "with MX-format experts at T = 1 ... 512")
     ap.add_argument("--variants", action="store_true",
                     help="also time the router options: sigmoid / raw routing on the "
                          "DeepSeek-V3-shaped router, capacity cuts on the Mixtral-shaped "
@@ -266,8 +270,8 @@ def time_variants(cfg, x, W, k, steps):
                            "capacity": cap, "dropped_pairs": int(np.clip(cnt - cap, 0, None).sum())}
         del wsm
     out["capacity_mixtral_t4096"] = cap_out
-    out["mxfp4_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128], 50)
-    out["mxfp8_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128], 50, fmt="mxfp8")
+    out["mxfp4_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128, 512], 50)
+    out["mxfp8_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128, 512], 50, fmt="mxfp8")
     return out
 
 
@@ -516,9 +520,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_check:
         copy_check(args.copy_check)
+    if args.workload in MX_WORKLOADS:
+        res = time_mx_decode(list(NAMED["gpt_oss"].t_sweep), args.decode_iters,
+                             fmt=MX_WORKLOADS[args.workload])
+        print(json.dumps({"workload": args.workload, "T": res}), flush=True)
+        return
     if args.workload != "all":
         if args.workload not in WORKLOADS:
-            sys.exit(f"bench.py: unknown workload {args.workload}; one of {', '.join(WORKLOADS)}")
+            sys.exit(f"bench.py: unknown workload {args.workload}; one of "
+                     f"{', '.join(list(WORKLOADS) + list(MX_WORKLOADS))}")
         fig = run_workload(args.workload, args.steps, args.warmup, args.decode_iters)
         print(json.dumps({"workload": args.workload, **fig}), flush=True)
         return

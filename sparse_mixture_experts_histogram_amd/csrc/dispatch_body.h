@@ -101,7 +101,7 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
     __syncthreads();
   }
   // Row-tile list only: entry 1 + i is row tile i (in group order); a kernel
-  // reads entry L as row tile L % mtot of column tile L / mtot.
+  // reads entry L as column tile L % n_tiles of row tile L / n_tiles.
   const int entries = c.row_list ? mtot : total;
   for (int L = first; L < entries; L += stride) {
     const int mL = c.row_list ? L : L / c.n_tiles;  // row tile "slot"

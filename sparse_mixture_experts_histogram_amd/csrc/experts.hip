@@ -672,9 +672,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(GemmArgs a) {
   static_assert((D - 1) * NDMA <= 63, "vmcnt range");
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
-  const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
-  Tile tl = uniform_tile(a.tiles[1 + L % mtot]);
-  tl.n0 = (L / mtot) * BN;
+  const int ncol = __builtin_amdgcn_readfirstlane(a.tiles[0].m_end);  // column tile fastest
+  Tile tl = uniform_tile(a.tiles[1 + L / ncol]);
+  tl.n0 = (L % ncol) * BN;
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
   const int K = sh ? a.K_s : a.K_r;
@@ -804,9 +804,9 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
   constexpr int U = 2;    // 128-k units per batch of loads
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
-  const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
-  Tile tl = uniform_tile(a.tiles[1 + L % mtot]);
-  tl.n0 = (L / mtot) * (16 * FG);
+  const int ncol = __builtin_amdgcn_readfirstlane(a.tiles[0].m_end);  // column tile fastest
+  Tile tl = uniform_tile(a.tiles[1 + L / ncol]);
+  tl.n0 = (L % ncol) * (16 * FG);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
   const int K = sh ? a.K_s : a.K_r;
@@ -978,9 +978,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   static_assert(EB == 4 || EB == 8, "FP4 or FP8 elements");
   const int L = tile_of_block(a.tiles);
   if (L < 0) return;
-  const int mtot = __builtin_amdgcn_readfirstlane(a.tiles[0].m0);
-  Tile tl = uniform_tile(a.tiles[1 + L % mtot]);
-  tl.n0 = (L / mtot) * (16 * NW);
+  const int ncol = __builtin_amdgcn_readfirstlane(a.tiles[0].m_end);  // column tile fastest
+  Tile tl = uniform_tile(a.tiles[1 + L / ncol]);
+  tl.n0 = (L % ncol) * (16 * NW);
   const bool sh = tl.g >= a.E;
   const int N = sh ? a.N_s : a.N_r;
   const int K = sh ? a.K_s : a.K_r;

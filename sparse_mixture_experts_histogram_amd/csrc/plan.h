@@ -53,7 +53,7 @@ struct GemmShape {
   int n_tiles;            // column tiles of the widest group
   int64_t max_row_tiles;  // upper bound of row tiles over all groups
   int64_t max_tiles;      // upper bound of (row tile, column tile) pairs
-  bool row_list;          // schedule lists row tiles only (column tile = L / rows)
+  bool row_list;          // schedule lists row tiles only (column tile = L % column tiles)
   int n_fastest;          // within a schedule chunk: 0 = row tile fastest, 1 = column
   int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
   int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
