@@ -21,15 +21,16 @@ static int prefill_rows(const moe_desc* d) {
   return pairs >= 384LL * d->E ? 256 : pairs <= 32LL * d->E ? 64 : 128;
 }
 // The streaming kernels use 16-row tiles of 16 (bf16) or 32 (MXFP4) columns;
-// MXFP4 layers with at least one (token, expert) pair per expert and a
+// MXFP4 layers with at least one (token, expert) pair per four experts and a
 // reduction of at most kMxLdsMaxK use the LDS-staged kernel's wider tiles
-// (measured on the gpt-oss-shaped layer: faster from 32 tokens on, slower
-// at 1).
+// (measured on the gpt-oss-shaped layer, with the LDS kernel's cached code
+// copies: T=8 0.140 -> 0.128 ms, T=16 0.212 -> 0.187 ms, T=32 alike; T=1
+// slower, 0.050 -> 0.056 ms).
 static bool streaming(int kind) {
   return kind == KIND_BF16_DECODE || kind == KIND_MXFP4 || kind == KIND_MXFP8;
 }
 static bool mx_lds(const moe_desc* d, int K) {
-  return (int64_t)d->T * d->k >= d->E && K <= kMxLdsMaxK;
+  return 4 * (int64_t)d->T * d->k >= d->E && K <= kMxLdsMaxK;
 }
 static int down_k(const moe_desc* d) {
   return d->n_shared && d->ffn_shared > d->ffn ? d->ffn_shared : d->ffn;

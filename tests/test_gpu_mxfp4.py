@@ -22,9 +22,9 @@ from moe_inputs import NAMED, generate, tables
 pytestmark = pytest.mark.gpu
 
 # Two kernels run MXFP4 experts: the direct-load one (fewer (token, expert)
-# pairs than experts, or K above 3072) and the LDS-staged one (16 x 128 up/gate
-# tiles, 16 x 64 down tiles, K in stages of 256 through a 3-slot ring).
-# mx_one_token and the gpt-oss T=1 and T=8 layers take the first;
+# pairs than a quarter of the experts, or K above 3072) and the LDS-staged one
+# (16 x 128 up/gate tiles, 16 x 64 down tiles, K in stages of 256 through a
+# 3-slot ring).  mx_few_pairs and the gpt-oss T=1 layer take the first;
 # mx_long_k takes it for up/gate only; the rest take the second: mx_ragged
 # and mx_shared with partial 128-feature tiles, mx_stages with 5 and 4
 # stages (the ring's two tail forms), mx_k2880 with a last stage of 2 blocks.
@@ -39,6 +39,7 @@ SMALL = {c.name: c for c in [
     custom("mx_k2880", 154, T=40, d=2880, E=4, k=2, ffn=2880),
     custom("mx_stages", 155, T=64, d=1280, E=8, k=2, ffn=1024),
     custom("mx_long_k", 156, T=24, d=4096, E=4, k=2, ffn=128),
+    custom("mx_few_pairs", 157, T=3, d=2880, E=32, k=2, ffn=384),
 ]}
 
 
