@@ -226,6 +226,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[UPGATE ? 2 : 1][TN][
   char* outb = (char*)a.out + (int64_t)split * a.split_stride * ES;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    if (row0 + 32 * j >= tl.m_end) break;  // row groups past the tile's last row
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -272,7 +273,6 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   constexpr int NS = UPGATE ? 2 : 1;                  // up and gate, or down
   constexpr int WB = WROWS / (8 * NW);                // 1 KB blocks per wave and stage
   constexpr int XB = BM / (8 * NW);
-  constexpr int NDMA = WB + XB;                       // DMA instructions per wave and stage
   static_assert(WB >= 1 && XB >= 1 && (!UPGATE || WB % 2 == 0), "tile shape");
   static_assert(NSW >= 2 && NSW <= 4 && NSX >= 2 && NSX <= 3, "stages");
 
@@ -383,10 +383,13 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 #pragma unroll
   for (int i = 0; i < XB; ++i)
     if (tl.m0 + 8 * (wave + NW * i) < tl.m_end) xlive |= 1u << i;
-  auto dma_x = [&](int kt_local, uint16_t* lx) {
+  // Token copies of the first XBL blocks per wave (XBL < XB: the blocks of
+  // 32-row groups past the tile's last row are not copied at all).
+  auto dma_x = [&](auto xblc, int kt_local, uint16_t* lx) {
+    constexpr int XBL = decltype(xblc)::value;
     const int s = kt_local - pad;
     const uint32_t koff = s < 0 ? 0u : (uint32_t)(kb + s) * (BK * 2);
-    dma_tile_live<XB, NW, kPolX>(s < 0 ? rzero : rx, rzero, xlive, koff, xoff, lx, wave);
+    dma_tile_live<XBL, NW, kPolX>(s < 0 ? rzero : rx, rzero, xlive, koff, xoff, lx, wave);
   };
 
   const int wn = wave % NWN, wm = wave / NWN;
@@ -400,6 +403,19 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][i][j][r] = 0.f;
 
+  // The main loop for LB live 32-row groups of the wave tile: MFMAs,
+  // fragment reads and token copies of the groups past the tile's last row
+  // are left out (their accumulators stay zero and are never stored).  When
+  // every wave spans all BM rows (WM == BM) all waves share one LB, chosen
+  // per tile below among TM compiled forms, so no branch enters the
+  // scheduled slab code; otherwise LB = TM.
+  auto main_loop = [&](auto lbc) {
+  constexpr int LB = decltype(lbc)::value;
+  static_assert(LB >= 1 && LB <= TM, "live row groups");
+  constexpr int XBL = XB * LB / TM;                 // token copy blocks per wave
+  static_assert(LB == TM || XB == TM, "token blocks follow the 32-row groups");
+  constexpr int NDL = WB + XBL;                     // DMA instructions per wave and stage
+
   // Fragment read offsets (elements) of k-step 0 of a slab: lane l reads row
   // (l % 32) of sub-tile 0 at chunk l / 32; the other sub-tiles are whole
   // 32-row blocks further.  Chunk 2 kk + c of a row sits at the slot of chunk
@@ -410,7 +426,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   auto fload = [&](const uint16_t* lw, const uint16_t* lx, int kk, u32x4* fx, u32x4 (*fw)[TN]) {
     const int ox = fxo ^ (kk << 4), ow = fwo ^ (kk << 4);
 #pragma unroll
-    for (int j = 0; j < TM; ++j) fx[j] = *(const u32x4*)(&lx[ox + j * 32 * BK]);
+    for (int j = 0; j < LB; ++j) fx[j] = *(const u32x4*)(&lx[ox + j * 32 * BK]);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -423,26 +439,32 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[s][i][j] = mfma32(fw[s][i], fx[j], acc[s][i][j]);
+        for (int j = 0; j < LB; ++j) acc[s][i][j] = mfma32(fw[s][i], fx[j], acc[s][i][j]);
   };
-  constexpr int NF = TM + NS * TN;   // fragment reads per k-step
-  constexpr int NMF = NS * TN * TM;  // MFMAs per k-step
-  // DMAs issued during k-steps 0, 1 and 2 of a slab: over kSpread k-steps,
-  // at most one per MFMA of a k-step
-  constexpr int kSpread = (NDMA + NMF - 1) / NMF < 2 ? 2 : (NDMA + NMF - 1) / NMF;
-  static_assert(kSpread <= 3, "DMAs fit three k-steps");
-  constexpr int ND0 = (NDMA + kSpread - 1) / kSpread;
-  constexpr int ND1 = kSpread >= 2 ? (NDMA - ND0 + kSpread - 2) / (kSpread - 1) : 0;
-  constexpr int ND2 = NDMA - ND0 - ND1;
-  static_assert(NMF >= NF && NMF >= ND0 && NMF >= ND1 && NMF >= ND2, "pipeline shape");
-  // Issue order for one k-step: MFMAs one by one, each followed by one
-  // fragment read (the first NF) and one DMA (the first nd).
+  constexpr int NF = LB + NS * TN;   // fragment reads per k-step
+  constexpr int NMF = NS * TN * LB;  // MFMAs per k-step
+  // DMAs issued during k-steps 0, 1 and 2 of a slab: over kSpread k-steps
+  // (at most three), about one per MFMA of a k-step where they fit
+  constexpr int kSpreadRaw = (NDL + NMF - 1) / NMF;
+  constexpr int kSpread = kSpreadRaw < 2 ? 2 : kSpreadRaw > 3 ? 3 : kSpreadRaw;
+  constexpr int ND0 = (NDL + kSpread - 1) / kSpread;
+  constexpr int ND1 = kSpread >= 2 ? (NDL - ND0 + kSpread - 2) / (kSpread - 1) : 0;
+  constexpr int ND2 = NDL - ND0 - ND1;
+  static_assert(LB < TM || (NMF >= NF && NMF >= ND0 && NMF >= ND1 && NMF >= ND2),
+                "pipeline shape of a whole tile");
+  // Issue order for one k-step: MFMAs one by one, each followed by its
+  // share of the fragment reads and DMAs (with at least as many MFMAs as
+  // either: one each after the first NF and nd MFMAs).
   auto pipeline = [&](int nd) {
 #pragma unroll
     for (int r = 0; r < NMF; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (r < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (r < nd) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      const int nr = NF / NMF + (r < NF % NMF ? 1 : 0);
+#pragma unroll
+      for (int q = 0; q < nr; ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int ndr = nd / NMF + (r < nd % NMF ? 1 : 0);
+#pragma unroll
+      for (int q = 0; q < ndr; ++q) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
   };
   auto barrier = [&]() {
@@ -465,15 +487,15 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
   // NSW - 2 whole slabs; with a longer weight ring the tokens of J + 1
   // (issued in slab J + 2 - NSX, before that slab's weight copies), then
   // NSX - 2 whole slabs.
-  constexpr int WAIT = NSX == NSW ? (NSW - 2) * NDMA : NWI + (NSX - 2) * NDMA;
+  constexpr int WAIT = NSX == NSW ? (NSW - 2) * NDL : NWI + (NSX - 2) * NDL;
   static_assert(WAIT <= 63, "vmcnt range");
   auto dma = [&](int kt_w, uint16_t* lw, int kt_x, uint16_t* lx) {
     if constexpr (NSX < NSW) {
-      dma_x(kt_x, lx);
+      dma_x(std::integral_constant<int, XBL>{}, kt_x, lx);
       dma_w(kt_w, lw);
     } else {
       dma_w(kt_w, lw);
-      dma_x(kt_x, lx);
+      dma_x(std::integral_constant<int, XBL>{}, kt_x, lx);
     }
   };
   // Wait until this wave's copies of the next slab have landed (and every
@@ -597,6 +619,38 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 #undef MOE_WB
 #undef MOE_XB
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the re-fetches
+  }
+  };  // main_loop
+  if constexpr (WM == BM) {
+    const int lb = (min(BM, tl.m_end - tl.m0) + 31) >> 5;
+    if constexpr (TM == 4) {
+      switch (lb) {
+        case 1: main_loop(std::integral_constant<int, 1>{}); break;
+        case 2: main_loop(std::integral_constant<int, 2>{}); break;
+        case 3: main_loop(std::integral_constant<int, 3>{}); break;
+        default: main_loop(std::integral_constant<int, 4>{}); break;
+      }
+    } else if constexpr (TM == 2) {
+      if (lb == 1)
+        main_loop(std::integral_constant<int, 1>{});
+      else
+        main_loop(std::integral_constant<int, 2>{});
+    } else if constexpr (TM == 8) {
+      switch (lb) {
+        case 1: main_loop(std::integral_constant<int, 1>{}); break;
+        case 2: main_loop(std::integral_constant<int, 2>{}); break;
+        case 3: main_loop(std::integral_constant<int, 3>{}); break;
+        case 4: main_loop(std::integral_constant<int, 4>{}); break;
+        case 5: main_loop(std::integral_constant<int, 5>{}); break;
+        case 6: main_loop(std::integral_constant<int, 6>{}); break;
+        case 7: main_loop(std::integral_constant<int, 7>{}); break;
+        default: main_loop(std::integral_constant<int, 8>{}); break;
+      }
+    } else {
+      main_loop(std::integral_constant<int, TM>{});
+    }
+  } else {
+    main_loop(std::integral_constant<int, TM>{});
   }
 
   if (piece >= 0) {  // a K piece of a last-round tile: accumulators to a.part
@@ -1357,6 +1411,9 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
                                                                     P.down.stream_w);
   else if (P.down.bm == 64)
     launch_gemm<64, 256, 64, 64, false, 2, 2>(grid, s, down_args(P, x), P.down.stream_w);
+  else if (P.down.all_rows)
+    launch_gemm<256, 256, 256, 64, false, kWStages256, kXStages256>(grid, s, down_args(P, x),
+                                                                   P.down.stream_w);
   else
     launch_gemm<256, 256, kDown256WM, kDown256WN, false, kWStages256, kXStages256>(
         grid, s, down_args(P, x), false);

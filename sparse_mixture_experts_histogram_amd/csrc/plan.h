@@ -59,6 +59,7 @@ struct GemmShape {
   int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
   int stream_w;           // weight bursts non-temporal (prefill kernels, 128-row tiles)
   int sk_cus;             // last-round split over this many workgroup slots (0: off)
+  int all_rows;           // 256-row tiles whose waves each span all rows (prefill)
 };
 
 struct Plan {
