@@ -8,17 +8,25 @@
 // tensors), "Mixture of Experts Explained: Routers, Active Parameters and
 // VRAM" (gated three-matrix feed-forward block).
 //
-// bf16 kernel: one workgroup (4 waves) computes a tile of BN output columns
-// by BM grouped rows with 32x32x16 bf16 MFMAs and fp32 accumulation.  The
-// MFMA "A" operand is the weight tile (rows = output features) and "B" is the
-// token tile, so each lane ends with 4 consecutive output features of one
-// token, which it stores as one 8-byte (bf16 h) or 16-byte (fp32 out) write.
-// Both operands are K-contiguous in memory and staged through LDS in 64-wide
-// K slabs (one 128-byte line per tile row), copied by global_load_lds_dwordx4
-// in 1 KB bursts of 8 whole rows, into a ring of 2-3 stages, with the 16-byte
-// chunks of a row XOR-swizzled so that the lanes of each ds_read_b128 phase
-// hit distinct banks.  Fragments of the next k-step are read from LDS while
-// the current MFMAs run.
+// Kernel families (the plan picks one per layer):
+// - gemm_bf16_kernel (prefill): one workgroup (4 waves) computes a tile of
+//   BN output columns by BM = 64, 128 or 256 grouped rows with 32x32x16 bf16
+//   MFMAs and fp32 accumulation.  The MFMA "A" operand is the weight tile
+//   (rows = output features) and "B" the token tile.  Both operands are
+//   K-contiguous in memory and staged through LDS in 64-wide K slabs (one
+//   128-byte line per tile row), copied by buffer_load_dwordx4 ... lds in
+//   1 KB bursts of 8 whole rows into separate weight and token rings, with
+//   the 16-byte chunks of a row XOR-swizzled so that the lanes of each
+//   ds_read_b128 phase hit distinct banks.  Fragments of the next k-step are
+//   read from LDS while the current MFMAs run.  When every wave spans all
+//   rows of the tile, the tile runs the compiled form for its count of live
+//   32-row groups.  A down GEMM with a long reduction splits its last,
+//   partly filled round of tiles along K (gemm_fixup_kernel adds the pieces).
+// - gemm_bf16_stream_kernel (decode): 16 x 16 tiles streaming the touched
+//   experts' weights, the four waves splitting K.
+// - gemm_mx_stream_kernel / gemm_mx_lds_kernel: MXFP4 and MXFP8 expert
+//   weights widened to bf16 in registers.
+// - gemm_f32_kernel: the float32 layer.
 // The up/gate tile holds the up and the gate rows of the same features, so
 // SwiGLU is applied in registers before h is written.
 //
