@@ -91,6 +91,9 @@ __device__ __forceinline__ int group_of_slot(const int* mbase, int G, int mL) {
 // workgroup; a global thread index and the grid's thread count when several
 // workgroups share the work); the thread with first == 0 writes the header.
 // Every workgroup builds the whole row-tile table in its own LDS.
+// RL: the schedule is known to be a row-tile list (c.row_list set), so the
+// code of the other layout is left out of the kernel.
+template <bool RL = false>
 __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, const int* mbase, int G, int mtot,
                             TileCfg c, Tile* tiles, int* rt_tab, int first, int stride) {
   const int total = mtot * c.n_tiles;
@@ -102,15 +105,17 @@ __device__ __forceinline__ void build_tiles(const int* goff, const int* gsize, c
   }
   // Row-tile list only: entry 1 + i is row tile i (in group order); a kernel
   // reads entry L as column tile L % n_tiles of row tile L / n_tiles.
-  const int entries = c.row_list ? mtot : total;
+  const bool rl = RL || c.row_list;
+  const int entries = rl ? mtot : total;
   for (int L = first; L < entries; L += stride) {
-    const int mL = c.row_list ? L : L / c.n_tiles;  // row tile "slot"
+    const int mL = rl ? L : L / c.n_tiles;  // row tile "slot"
     const int g = tab ? rt_tab[mL] : group_of_slot(mbase, G, mL);
-    if (c.row_list) {
+    if (rl) {
       const int m0 = goff[g] + (mL - mbase[g]) * c.bm;
       tiles[1 + L] = Tile{g, m0, min(m0 + c.bm, goff[g] + gsize[g]), 0};
       continue;
     }
+    if constexpr (RL) continue;
     const int Mg = (gsize[g] + c.bm - 1) / c.bm;
     const int local = L - mbase[g] * c.n_tiles;
     const int sn = Mg >= 32 ? 1 : 32 / Mg;
@@ -189,7 +194,8 @@ __device__ __forceinline__ void column_scan(int32_t* blk_hist, int nblk, int E, 
 // LDS, then the schedules, the placement of the pairs and the shared rows,
 // over thread range (first, stride) as in build_tiles.  ONE_BLOCK: the
 // block offsets are zero (a single token block), so blk_hist is not read.
-template <bool ONE_BLOCK>
+// RL: both schedules are row-tile lists (see build_tiles).
+template <bool ONE_BLOCK, bool RL = false>
 __device__ __forceinline__ void layout_and_place(
     const int32_t* idx, const int32_t* blk_hist, const int32_t* blk_rank, int T, int k, int E,
     int n_sh, int cap, const int* gsize, int32_t* offsets, int32_t* sorted_token,
@@ -218,8 +224,8 @@ __device__ __forceinline__ void layout_and_place(
   if (tid <= G) mb_dn[tid] = tid < G ? exd : mtot_d;
   __syncthreads();
   for (int g = first; g <= G; g += stride) offsets[g] = goff[g];
-  build_tiles(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab, first, stride);
-  build_tiles(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab, first, stride);
+  build_tiles<RL>(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab, first, stride);
+  build_tiles<RL>(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab, first, stride);
 
   // 4. stable placement of the routed pairs, kPlace pairs per thread at a
   // time (their index and rank loads, then their block-offset loads, are
@@ -278,7 +284,8 @@ __device__ __forceinline__ void layout_and_place(
 // blk_rank are LDS arrays, hence no __restrict__); the block's exclusive
 // offsets are then all zero and there is no column scan.  Pair indices fit
 // in 32 bits (the descriptor check bounds T * (k + n_shared) below 2^31).
-template <bool ONE_BLOCK>
+// RL: both schedules are row-tile lists.
+template <bool ONE_BLOCK, bool RL = false>
 __device__ __forceinline__ void dispatch_body(
     const int32_t* idx, int32_t* blk_hist, const int32_t* blk_rank,
     int T, int k, int E, int n_sh, int nblk, int cap, int32_t* counts, int32_t* offsets,
@@ -299,7 +306,7 @@ __device__ __forceinline__ void dispatch_body(
   }
   if (tid >= E && tid < G) gsize[tid] = T;
   __syncthreads();
-  layout_and_place<ONE_BLOCK>(idx, blk_hist, blk_rank, T, k, E, n_sh, cap, gsize, offsets,
+  layout_and_place<ONE_BLOCK, RL>(idx, blk_hist, blk_rank, T, k, E, n_sh, cap, gsize, offsets,
                               sorted_token, slot_row, tiles_up, cu, tiles_down, cd, tid,
                               kDispatchThreads);
 }

@@ -184,87 +184,67 @@ __device__ __forceinline__ void store_partial(f32x16 (&acc)[NS][TN][TM], float* 
                              acc[s][i][j][4 * q + 3]);
       }
 }
-// acc (+)= one stored partial (LOAD: acc = partial; else acc += partial).
-template <int NS, int TN, int TM, bool LOAD>
-__device__ __forceinline__ void add_partial(f32x16 (&acc)[NS][TN][TM], const float* src, int wave,
-                                            int lane) {
-  constexpr int NACC = NS * TN * TM;
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const float4* p =
-            (const float4*)(src + ((wave * NACC + (s * TN + i) * TM + j) * 64 + lane) * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 u = p[q];
-          if (LOAD) {
-            acc[s][i][j][4 * q] = u.x;
-            acc[s][i][j][4 * q + 1] = u.y;
-            acc[s][i][j][4 * q + 2] = u.z;
-            acc[s][i][j][4 * q + 3] = u.w;
-          } else {
-            acc[s][i][j][4 * q] += u.x;
-            acc[s][i][j][4 * q + 1] += u.y;
-            acc[s][i][j][4 * q + 2] += u.z;
-            acc[s][i][j][4 * q + 3] += u.w;
-          }
-        }
-      }
-}
-
 // D[n = feature][m = row]: lane holds row (lane & 31) and, for q = 0..3,
 // features 8q + 4*(lane>>5) + 0..3 of each 32x32 sub-tile.  Outputs are
 // written through LDS so that every store is a 16-byte piece of a whole
-// row: each wave stages 32 rows x WN features of its tile at a time in a
-// stage buffer of its own (row pitch padded by 16 bytes against bank
-// conflicts), then stores them as 16-byte pieces, consecutive lanes along
-// a row.
-template <int WM, int WN, int TN, int TM, bool UPGATE>
-__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[UPGATE ? 2 : 1][TN][TM], const Tile& tl,
-                                              int N, const GemmArgs& a, int split, char* st,
-                                              int wm, int wn, int lane) {
+// row: a wave stages 32 rows x WN features at a time in a stage buffer of
+// its own (row pitch padded by 16 bytes against bank conflicts), then stores
+// them as 16-byte pieces, consecutive lanes along a row.
+// store_rows32 writes one such 32-row group starting at row0 (rows at or
+// past m_end and columns at or past N are not written); get(s, i, r) is
+// element r of the accumulator of operand s (up/gate: 0 up, 1 gate) and
+// 32-column sub-tile i.
+template <int WN, int TN, bool UPGATE, class Get>
+__device__ __forceinline__ void store_rows32(Get get, int row0, int col0, int m_end, int N,
+                                             const GemmArgs& a, int split, char* st, int lane) {
   constexpr int ES = UPGATE ? 2 : 4;                  // output element bytes
   constexpr int RB = WN * ES, PITCH = RB + 16;        // staged row bytes, LDS pitch
   constexpr int LPR = RB / 16;                         // 16-byte pieces per staged row
   static_assert(RB % 16 == 0, "epilogue shape");
-  const int row0 = tl.m0 + wm * WM, col0 = tl.n0 + wn * WN;
   char* outb = (char*)a.out + (int64_t)split * a.split_stride * ES;
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      char* dst = st + (lane & 31) * PITCH + (i * 32 + 8 * q + 4 * (lane >> 5)) * ES;
+      if (UPGATE) {
+        uint16_t hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hv[r] = f32_to_bf16(silu_mul(get(1, i, 4 * q + r), get(0, i, 4 * q + r)));
+        uint2 pk;
+        pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+        *(uint2*)dst = pk;
+      } else {
+        *(float4*)dst = make_float4(get(0, i, 4 * q + 0), get(0, i, 4 * q + 1),
+                                    get(0, i, 4 * q + 2), get(0, i, 4 * q + 3));
+      }
+    }
+  }
+#pragma unroll
+  for (int id0 = 0; id0 < 32 * LPR; id0 += 64) {
+    const int id = id0 + lane, r = id / LPR, cb = (id % LPR) * 16;
+    if (id < 32 * LPR) {
+      const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
+      const int row = row0 + r, col = col0 + cb / ES;
+      if (row < m_end && col < N) *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
+    }
+  }
+}
+
+// The wave's whole WM x WN tile, 32-row group by 32-row group (groups at or
+// past the tile's last row are skipped).
+template <int WM, int WN, int TN, int TM, bool UPGATE>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[UPGATE ? 2 : 1][TN][TM], const Tile& tl,
+                                              int N, const GemmArgs& a, int split, char* st,
+                                              int wm, int wn, int lane) {
+  const int row0 = tl.m0 + wm * WM, col0 = tl.n0 + wn * WN;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     if (row0 + 32 * j >= tl.m_end) break;  // row groups past the tile's last row
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        char* dst = st + (lane & 31) * PITCH + (i * 32 + 8 * q + 4 * (lane >> 5)) * ES;
-        if (UPGATE) {
-          uint16_t hv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            hv[r] = f32_to_bf16(silu_mul(acc[1][i][j][4 * q + r], acc[0][i][j][4 * q + r]));
-          uint2 pk;
-          pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-          pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *(uint2*)dst = pk;
-        } else {
-          *(float4*)dst = make_float4(acc[0][i][j][4 * q + 0], acc[0][i][j][4 * q + 1],
-                                      acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3]);
-        }
-      }
-    }
-#pragma unroll
-    for (int id0 = 0; id0 < 32 * LPR; id0 += 64) {
-      const int id = id0 + lane, r = id / LPR, cb = (id % LPR) * 16;
-      if (id < 32 * LPR) {
-        const u32x4 v = *(const u32x4*)(st + r * PITCH + cb);
-        const int row = row0 + j * 32 + r, col = col0 + cb / ES;
-        if (row < tl.m_end && col < N)
-          *(u32x4*)(outb + ((int64_t)row * a.ldo + col) * ES) = v;
-      }
-    }
+    store_rows32<WN, TN, UPGATE>([&](int s, int i, int r) { return acc[s][i][j][r]; },
+                                 row0 + 32 * j, col0, tl.m_end, N, a, split, st, lane);
   }
 }
 
@@ -682,28 +662,58 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_bf16_kernel(G
 
 // Adds the K pieces of each last-round tile of a split GEMM launch (see
 // sk_layout), in piece order, and writes the tile as the GEMM epilogue does
-// (SwiGLU and bf16 h for up/gate, float32 for down).  Workgroup t handles
-// split tile dp + t; the piece accumulators use the GEMM's register layout.
+// (SwiGLU and bf16 h for up/gate, float32 for down).  The piece
+// accumulators use the GEMM's register layout.  Workgroup b handles GEMM
+// wave b % NW of split tile dp + b / NW; its wave j takes that GEMM wave's
+// 32-row group j, so a tile is spread over NW * TM waves on several CUs (one
+// workgroup per tile, walking its row groups in turn, left most CUs idle
+// while the few last-round tiles were summed).
 template <int BM, int BN, int WM, int WN, bool UPGATE>
-__global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fixup_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * (WM / 32)) void gemm_fixup_kernel(GemmArgs a) {
   constexpr int NWN = BN / WN, NWM = BM / WM, NW = NWN * NWM;
   constexpr int TN = WN / 32, TM = WM / 32, NS = UPGATE ? 2 : 1;
+  constexpr int NACC = NS * TN * TM;
   constexpr int PITCH = WN * (UPGATE ? 2 : 4) + 16;
-  constexpr size_t PIECE = (size_t)NW * NS * TN * TM * 1024;  // floats per piece
-  __shared__ __attribute__((aligned(16))) char stage[NW][32 * PITCH];
+  constexpr size_t PIECE = (size_t)NW * NACC * 1024;  // floats per piece
+  __shared__ __attribute__((aligned(16))) char stage[TM][32 * PITCH];
   const SkLayout sk = sk_layout(a.tiles[0].g, a.sk_cus, min(a.K_r, a.K_s) / BK);
-  const int t = blockIdx.x;
+  const int t = blockIdx.x / NW, gw = blockIdx.x % NW;  // tile, GEMM wave
   if (t >= sk.r) return;
   const Tile tl = uniform_tile(a.tiles[1 + sk.dp + t]);
   const int N = tl.g >= a.E ? a.N_s : a.N_r;
   if (tl.n0 >= N) return;  // the GEMM wrote no pieces for it either
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  f32x16 acc[NS][TN][TM];
+  const int lane = threadIdx.x & 63, j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = gw / NWN, wn = gw % NWN;
+  const int row0 = tl.m0 + wm * WM + 32 * j;
+  if (row0 >= tl.m_end) return;
+  f32x16 acc[NS][TN];
   const float* base = a.part + (size_t)t * sk.s * PIECE;
-  add_partial<NS, TN, TM, true>(acc, base, wave, lane);
-  for (int j = 1; j < sk.s; ++j) add_partial<NS, TN, TM, false>(acc, base + j * PIECE, wave, lane);
-  tile_epilogue<WM, WN, TN, TM, UPGATE>(acc, tl, N, a, 0, stage[wave], wave / NWN, wave % NWN,
-                                        lane);
+  for (int p = 0; p < sk.s; ++p) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const float4* src = (const float4*)(base + p * PIECE +
+                                            ((gw * NACC + (s * TN + i) * TM + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 u = src[q];
+          if (p == 0) {
+            acc[s][i][4 * q] = u.x;
+            acc[s][i][4 * q + 1] = u.y;
+            acc[s][i][4 * q + 2] = u.z;
+            acc[s][i][4 * q + 3] = u.w;
+          } else {
+            acc[s][i][4 * q] += u.x;
+            acc[s][i][4 * q + 1] += u.y;
+            acc[s][i][4 * q + 2] += u.z;
+            acc[s][i][4 * q + 3] += u.w;
+          }
+        }
+      }
+  }
+  store_rows32<WN, TN, UPGATE>([&](int s, int i, int r) { return acc[s][i][r]; }, row0,
+                               tl.n0 + wn * WN, tl.m_end, N, a, 0, stage[j], lane);
 }
 
 // ---------------------------------------------------------------- decode
@@ -1347,8 +1357,8 @@ static void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a, bool stream
   if (a.sk_cus > 0) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, UPGATE, NSW, NSX, 0>),
                        dim3(grid.x + 8 + (unsigned)a.sk_cus), dim3(64 * nw), 0, s, a);
-    hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, UPGATE>), dim3((unsigned)a.sk_cus),
-                       dim3(64 * nw), 0, s, a);
+    hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, UPGATE>),
+                       dim3((unsigned)a.sk_cus * nw), dim3(64 * (WM / 32)), 0, s, a);
     return;
   }
   if (stream_w)

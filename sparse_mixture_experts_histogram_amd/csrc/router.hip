@@ -366,7 +366,9 @@ struct FusedDispatch {
 // kernels run once per layer on one or a few workgroups, and a kernel holding
 // every selection width and both tails was large enough for instruction
 // fetch to dominate its time.
-template <int EPL, bool FUSED>
+// FUSED: 0 no dispatch, 1 the dispatch, 2 the dispatch of two row-tile-list
+// schedules (the decode kernels' layout; the other layout's code left out).
+template <int EPL, int FUSED>
 __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     const float* __restrict__ part, int64_t plane, const float* __restrict__ bias, int mode, int T,
     int E, int k, int nblk, int nsplit, int32_t* idx_out, float* w_out, int32_t* blk_hist,
@@ -376,7 +378,10 @@ __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
   int32_t* sel = (int32_t*)(lds + kRouterTokens * ld);
   const int t0 = blockIdx.x * kRouterTokens;
   const float* src = part + (int64_t)t0 * ep;
-  for (int i = threadIdx.x; i < kRouterTokens * ep; i += blockDim.x) {
+  // rows of the block's tokens only (the selection reads no others): with a
+  // few tokens, one batch of loads per thread
+  const int nt = min(kRouterTokens, T - t0);
+  for (int i = threadIdx.x; i < nt * ep; i += blockDim.x) {
     float v[kMaxRouterSplit];
 #pragma unroll
     for (int q = 0; q < kMaxRouterSplit; ++q) v[q] = src[(q < nsplit ? q : 0) * plane + i];
@@ -398,14 +403,14 @@ __global__ __launch_bounds__(kDispatchThreads) void router_finish_kernel(
     __shared__ int32_t f_rank[kRouterTokens * kMaxTopK];
     router_tail<EPL>(lds, ld, sel, bias, mode, t0, T, E, k, idx_out, w_out, f_hist, f_rank);
     __syncthreads();
-    dispatch_body<true>(sel, f_hist, f_rank, T, k, E, fd.n_sh, nblk, fd.cap, fd.counts,
-                        fd.offsets, fd.sorted_token, fd.slot_row, fd.tiles_up, fd.cu,
-                        fd.tiles_down, fd.cd);
+    dispatch_body<true, FUSED == 2>(sel, f_hist, f_rank, T, k, E, fd.n_sh, nblk, fd.cap,
+                                    fd.counts, fd.offsets, fd.sorted_token, fd.slot_row,
+                                    fd.tiles_up, fd.cu, fd.tiles_down, fd.cd);
   }
 }
 
 // The finish kernel for E experts (and the fused dispatch or not).
-template <bool FUSED>
+template <int FUSED>
 hipError_t launch_finish(dim3 grid, size_t lds, hipStream_t s, const float* part, int64_t plane,
                          const float* bias, int mode, int T, int E, int k, int nblk, int nsplit,
                          int32_t* idx, float* w, int32_t* blk_hist, int32_t* blk_rank,
@@ -513,7 +518,7 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
       partial(router_wide_partial_kernel<8>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finish<false>(grid, (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
+    return launch_finish<0>(grid, (size_t)kRouterTokens * ld * 4 + sel_bytes, s, part,
                                 (int64_t)ngroups * P.rwide * ep, bias, P.route_mode, (int)D.T, D.E,
                                 D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank,
                                 FusedDispatch{});
@@ -542,10 +547,13 @@ hipError_t launch_router(const Plan& P, const void* x, const void* w_router, con
     if (e != hipSuccess) return e;
     const size_t flds = (size_t)kRouterTokens * ld * 4 + sel_bytes;
     const int64_t plane = (int64_t)P.nblk * kRouterTokens * ep;
+    if (fd.counts && fd.cu.row_list && fd.cd.row_list)
+      return launch_finish<2>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
+                              D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
     if (fd.counts)
-      return launch_finish<true>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
-                                 D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
-    return launch_finish<false>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
+      return launch_finish<1>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
+                              D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
+    return launch_finish<0>(grid, flds, s, part, plane, bias, P.route_mode, (int)D.T, D.E,
                                 D.k, (int)P.nblk, P.rsplit, idx, w, blk_hist, blk_rank, fd);
   }
   auto args = [&](auto kern) {
