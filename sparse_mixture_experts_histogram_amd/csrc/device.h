@@ -40,27 +40,22 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
 // One max step: v = max(v, v of the lane DPP control CTRL selects); lanes
 // without a source (or outside ROW_MASK) keep their own value.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xf, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xf, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+__device__ __forceinline__ uint32_t dpp_max_step32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
   return o > v ? o : v;
 }
 
 // Maximum over the 64 lanes, returned to every lane.  DPP row shifts by
 // 1, 2, 4, 8 leave each 16-lane row's maximum in its lane 15; row broadcasts
 // of lane 15 and lane 31 then carry it to lane 63, which is read out.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
-  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
-  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
-  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
-  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step32<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step32<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step32<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step32<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -67,6 +67,41 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   return before + x - v;
 }
 
+// block_excl_scan of three values at once (one pair of barriers for all
+// three); buf holds at least 3 * kDispatchThreads / 64 ints.
+__device__ __forceinline__ void block_excl_scan3(const int (&v)[3], int* buf, int (&ex)[3],
+                                                 int (&total)[3]) {
+  constexpr int NWV = kDispatchThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int y = __shfl_up(x[c], off);
+      if (lane >= off) x[c] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) buf[c * NWV + wave] = x[c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const int t = buf[c * NWV + w];
+      before += w < wave ? t : 0;
+      all += t;
+    }
+    total[c] = all;
+    ex[c] = before + x[c] - v[c];
+  }
+  __syncthreads();  // buf is free again
+}
+
 // Tile schedule of one grouped GEMM.  Group g has mt_g = ceil(size_g / bm)
 // row tiles and n_tiles column tiles; its entries are laid out in chunks of
 // about 32 tiles that hold every row tile of a few consecutive column tiles
@@ -201,7 +236,7 @@ __device__ __forceinline__ void layout_and_place(
     int n_sh, int cap, const int* gsize, int32_t* offsets, int32_t* sorted_token,
     int32_t* slot_row, Tile* tiles_up, TileCfg cu, Tile* tiles_down, TileCfg cd, int first,
     int stride) {
-  __shared__ int scan_buf[kDispatchThreads / 64];
+  __shared__ int scan_buf[3 * (kDispatchThreads / 64)];
   __shared__ int goff[kMaxGroups + 1];
   __shared__ int mb_up[kMaxGroups + 1];
   __shared__ int mb_dn[kMaxGroups + 1];
@@ -209,23 +244,38 @@ __device__ __forceinline__ void layout_and_place(
   const int tid = threadIdx.x;
   const int G = E + n_sh;
   // 2. group offsets; 3. row-tile bases of both schedules
-  int total;
   const int sz = tid < G ? gsize[tid] : 0;
-  const int ex = block_excl_scan(sz, scan_buf, &total);
-  if (tid < G) goff[tid] = ex;
-  if (tid == 0) goff[G] = total;
-  const int mu = tid < G ? (sz + cu.bm - 1) / cu.bm : 0;
-  int mtot_u;
-  const int exu = block_excl_scan(mu, scan_buf, &mtot_u);
-  if (tid <= G) mb_up[tid] = tid < G ? exu : mtot_u;
-  const int md = tid < G ? (sz + cd.bm - 1) / cd.bm : 0;
-  int mtot_d;
-  const int exd = block_excl_scan(md, scan_buf, &mtot_d);
-  if (tid <= G) mb_dn[tid] = tid < G ? exd : mtot_d;
+  const int vals[3] = {sz, tid < G ? (sz + cu.bm - 1) / cu.bm : 0,
+                       tid < G ? (sz + cd.bm - 1) / cd.bm : 0};
+  int ex[3], tot[3];
+  block_excl_scan3(vals, scan_buf, ex, tot);
+  const int mtot_u = tot[1], mtot_d = tot[2];
+  if (tid < G) goff[tid] = ex[0];
+  if (tid == 0) goff[G] = tot[0];
+  if (tid <= G) mb_up[tid] = tid < G ? ex[1] : mtot_u;
+  if (tid <= G) mb_dn[tid] = tid < G ? ex[2] : mtot_d;
   __syncthreads();
   for (int g = first; g <= G; g += stride) offsets[g] = goff[g];
-  build_tiles<RL>(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab, first, stride);
-  build_tiles<RL>(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab, first, stride);
+  if (RL && cu.bm == cd.bm) {
+    // Two row-tile lists of the same row tiles: each group writes its own
+    // entries of both (no group lookup per entry).
+    for (int g = first; g < G; g += stride) {
+      const int end = goff[g] + gsize[g];
+      for (int m = mb_up[g]; m < mb_up[g + 1]; ++m) {
+        const int m0 = goff[g] + (m - mb_up[g]) * cu.bm;
+        const Tile t{g, m0, min(m0 + cu.bm, end), 0};
+        tiles_up[1 + m] = t;
+        tiles_down[1 + m] = t;
+      }
+    }
+    if (first == 0) {
+      tiles_up[0] = Tile{mtot_u * cu.n_tiles, mtot_u, cu.n_tiles, 0};
+      tiles_down[0] = Tile{mtot_d * cd.n_tiles, mtot_d, cd.n_tiles, 0};
+    }
+  } else {
+    build_tiles<RL>(goff, gsize, mb_up, G, mtot_u, cu, tiles_up, rt_tab, first, stride);
+    build_tiles<RL>(goff, gsize, mb_dn, G, mtot_d, cd, tiles_down, rt_tab, first, stride);
+  }
 
   // 4. stable placement of the routed pairs, kPlace pairs per thread at a
   // time (their index and rank loads, then their block-offset loads, are

@@ -12,9 +12,9 @@
 // bf16 variant computes the logit tile with 16x16x32 bf16 MFMAs (exact bf16
 // products, fp32 accumulation); the K range is split across waves when E
 // leaves room for it and the partial tiles are summed in a fixed order.  Selection runs one
-// wave per token on 64-bit keys (order-preserving fp32 logit, then 2^32-1-e),
-// so a wave-wide max picks the largest logit and, among exact ties, the lowest
-// expert index.  Only the kept logits are needed for the weights:
+// wave per token on order-preserving uint32 keys of the fp32 scores: a
+// wave-wide max picks the largest score, and a ballot of the experts holding
+// it the lowest expert index among exact ties.  Only the kept logits are needed for the weights:
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), which equals renormalising the
 // full softmax (page "Mixture of Experts Explained...", section "Softmax
 // before or after the top-k step").
@@ -75,16 +75,22 @@ __device__ __forceinline__ void topk_block(const float* lg, int ld, const float*
     const int t = t0 + tl;
     if (t >= T) break;
     const float* lt = lg + tl * ld;
-    uint64_t key[EPL];
+    // Selection key of expert e = lane + 64 i: the order-preserving uint32 of
+    // its score; bit i of `live` marks an expert that exists and is not yet
+    // chosen.  Each pick takes the wave's largest live key and, among live
+    // keys equal to it, the lowest expert index (one ballot per i, lowest i
+    // first, then the lowest lane).
+    uint32_t key[EPL];
+    uint32_t live = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
+      key[i] = 0;
       if (e < E) {
         const float b = bias ? bias[e] : 0.0f;
         const float v = sig ? sigmoid_f32(lt[e]) + b : lt[e] + b;
-        key[i] = ((uint64_t)order_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-      } else {
-        key[i] = 0;
+        key[i] = order_key(v);
+        live |= 1u << i;
       }
     }
     // kept score of slot j: exp(v_j - v_0) (softmax numerator relative to
@@ -92,15 +98,19 @@ __device__ __forceinline__ void topk_block(const float* lg, int ld, const float*
     float v0 = 0.f, wsum = 0.f, my_w = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-      uint64_t m = 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) m = key[i] > m ? key[i] : m;
-      m = wave_max_u64(m);
+      uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (key[i] == m) key[i] = 0;
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
-      const float v = order_key_inv((uint32_t)(m >> 32));
+        if (((live >> i) & 1u) && key[i] > m) m = key[i];
+      m = wave_max_u32(m);
+      int e = -1;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const uint64_t hit = __ballot(((live >> i) & 1u) && key[i] == m);
+        if (e < 0 && hit) e = 64 * i + __builtin_ctzll(hit);
+      }
+      if (lane == (e & 63)) live &= ~(1u << (e >> 6));
+      const float v = order_key_inv(m);
       if (j == 0) v0 = v;
       const float sc = sig ? sigmoid_f32(lt[e]) : expf(v - v0);
       wsum += sc;
