@@ -1019,9 +1019,11 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
 // g of feature row r's block j, widened with the row's block scale, and
 // token row r.  16-byte chunks sit XOR-swizzled in LDS (codes: chunk c of
 // row r at c ^ (r / 2) % 8; tokens: chunk c at c ^ r % 16) so fragment
-// reads spread over the banks.  Blocks past K copy a clamped chunk and
-// their codes are zeroed; waves past N (a partial tile) re-read the last
-// row and store nothing.  Needs K a multiple of 64 and at most kMxLdsMaxK.
+// reads spread over the banks.  Blocks past K copy a clamped chunk of
+// codes and zeros for the tokens, so they add nothing (a zero token times a
+// finite code; a NaN code or scale there is one of the last live block's,
+// which makes the sum NaN anyway); waves past N (a partial tile) re-read
+// the last row and store nothing.  Needs K a multiple of 64 and at most kMxLdsMaxK.
 // EB = 8 is the MXFP8 form: E4M3 codes, one per byte, so a row's stage is
 // 256 bytes (a copy moves 4 rows, chunk c of row r at slot c ^ r % 16), a
 // lane reads 8 bytes of its block and widens them with
@@ -1067,22 +1069,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lx0[XS], lx1[XS], lx2[XS];
   __shared__ __attribute__((aligned(1024))) uint8_t lc0[CS], lc1[CS], lc2[CS];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[NS * SCS];
+  // E8M0 byte -> float32 scale 2^(byte - 127) (byte 0: 2^-127, a float32
+  // subnormal; byte 255: NaN), so a scale costs one LDS read instead of a
+  // shift, two compares and two selects per block
+  __shared__ float e8m0[256];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int b = threadIdx.x; b < 256; b += 64 * NW)
+    e8m0[b] = __uint_as_float(b == 0 ? 0x00400000u : b == 255 ? 0x7FC00000u : (uint32_t)b << 23);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & kLgkm0);  // written before the first barrier
 
   // token copy: instruction i of wave w fills 1 KB block b = w + NW i, rows
   // 2 b + l / 32; lane l takes LDS slot l % 32 of its row, global chunk
-  // slot ^ row % 16
-  const uint16_t* xsrc[XI];
+  // slot ^ row % 16.  The copies are buffer loads, and a chunk past K reads
+  // at offset tok_bytes (out of range): zeros, so the 32-k blocks past K add
+  // nothing whatever their (clamped) codes hold.
+  uint32_t xoffb[XI];
   int xchunk[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int xr = 2 * (wave + NW * i) + (lane >> 5);
     int xrow = tl.m0 + xr;
     xrow = xrow < tl.m_end ? xrow : tl.m_end - 1;
-    const int64_t xtok = a.sorted ? (int64_t)a.sorted[xrow] : (int64_t)xrow;
-    xsrc[i] = a.tok + xtok * a.ldt;
+    const uint32_t xtok = a.sorted ? (uint32_t)a.sorted[xrow] : (uint32_t)xrow;
+    xoffb[i] = xtok * (uint32_t)a.ldt * 2;
     xchunk[i] = (lane & 31) ^ (xr & 15);
   }
+  const __amdgpu_buffer_rsrc_t rx = buffer_of(a.tok, a.tok_bytes);
   // code copy: instruction i of a matrix holds feature rows 16 w + RPC i +
   // l / LPR; lane l takes slot l % LPR, the row's 16-byte chunk of the stage
   // slot ^ (row / 2) % 8 (FP4) or slot ^ row % 16 (FP8)
@@ -1125,10 +1137,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
     st = st < nst ? st : nst - 1;
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-      int c = 32 * st + xchunk[i];           // 8-k chunk along the token row
-      c = c < (K >> 3) ? c : (K >> 3) - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + c * 8),
-                                       LDS_PTR(lx + (wave + NW * i) * 512), 16, 0, 0);
+      const int c = 32 * st + xchunk[i];     // 8-k chunk along the token row
+      const uint32_t off = c < (K >> 3) ? xoffb[i] + (uint32_t)c * 16 : a.tok_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS_PTR(lx + (wave + NW * i) * 512), 16, off,
+                                               0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NS; ++q)
@@ -1149,7 +1161,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   auto compute = [&](int st, const uint16_t* xs, const uint8_t* lc) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool live = 8 * st + j < nb;
       const int xoff = r * 256 + (((4 * j + g) ^ r) << 3);
       const u32x4 fx = *(const u32x4*)(xs + xoff);
 #pragma unroll
@@ -1168,10 +1179,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
         const uint32_t byte = lsc[q * SCS + srow + bj];
         asm volatile("" ::: "memory");  // keep reads of different arrays apart (a
                                         // merged read carries no alias information)
-        w[0] = live ? w[0] : 0u;
-        w[1] = live ? w[1] : 0u;
-        const float scale =
-            __uint_as_float(byte == 0 ? 0x00400000u : byte == 255 ? 0x7FC00000u : byte << 23);
+        const float scale = e8m0[byte];
         u32x4 fa;
         if (EB == 4) {
           fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 0));
