@@ -1159,6 +1159,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int srow = (16 * wave + r) * nb;     // this lane's scale row in LDS
   auto compute = [&](int st, const uint16_t* xs, const uint8_t* lc) {
+    // the stage's 8 block scales of each matrix first: independent reads,
+    // then their table entries, instead of a two-read chain per block
+    uint32_t sbyte[NS][8];
+    float scl[NS][8];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sbyte[q][j] = lsc[q * SCS + srow + min(8 * st + j, nb - 1)];
+        asm volatile("" ::: "memory");  // no merged reads (they carry no alias information)
+      }
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) scl[q][j] = e8m0[sbyte[q][j]];
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int xoff = r * 256 + (((4 * j + g) ^ r) << 3);
@@ -1175,11 +1191,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
         } else {
           w = *(const u32x2*)(lc + base + (((2 * j + (g >> 1)) ^ r) << 4) + 8 * (g & 1));
         }
-        const int bj = min(8 * st + j, nb - 1);
-        const uint32_t byte = lsc[q * SCS + srow + bj];
         asm volatile("" ::: "memory");  // keep reads of different arrays apart (a
                                         // merged read carries no alias information)
-        const float scale = e8m0[byte];
+        const float scale = scl[q][j];
         u32x4 fa;
         if (EB == 4) {
           fa[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], scale, 0));
