@@ -61,6 +61,9 @@ SMALL = {c.name: c for c in [
     # routed experts' (pieces of unequal length), 16 tiles of 16 pieces
     custom("last_round_shared", 119, T=800, d=512, E=2, k=1, ffn=8192, n_shared=1,
            ffn_shared=8448, bias="normal", bias_var=0.5),
+    # the all-rows 256-row down form (experts of 128 to 384 rows: 300 each)
+    # with K >= 8192: 4 tiles of 16 pieces, added by the fixup's 8-wave form
+    custom("last_round_all_rows", 121, T=600, d=256, E=2, k=1, ffn=8192),
     NAMED["tiny_f32"],
 ]}
 
