@@ -272,15 +272,21 @@ def time_variants(cfg, x, W, k, steps):
     out["capacity_mixtral_t4096"] = cap_out
     out["mxfp4_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128, 512], 50)
     out["mxfp8_gpt_oss_decode"] = time_mx_decode([1, 8, 32, 128, 512], 50, fmt="mxfp8")
+    out["mxfp4_gpt_oss_decode_line_rows"] = time_mx_decode([1, 8, 32, 128, 512], 50,
+                                                           line_rows=True)
+    out["mxfp8_gpt_oss_decode_line_rows"] = time_mx_decode([1, 8, 32, 128, 512], 50,
+                                                           fmt="mxfp8", line_rows=True)
     return out
 
 
-def time_mx_decode(Ts, iters, fmt="mxfp4"):
+def time_mx_decode(Ts, iters, fmt="mxfp4", line_rows=False):
     """The gpt-oss-shaped layer (d=2880, 128 experts, top-4, ffn 2880) with
     MXFP4 (or, fmt="mxfp8", MXFP8) expert weights at decode batch sizes:
     per-iteration hipEvents before the first and after the last launch, L2
     and MALL flushed by a 1 GiB read between iterations, median of `iters`;
-    HBM fraction on the touched experts' code and scale bytes."""
+    HBM fraction on the touched experts' code and scale bytes.  line_rows:
+    code rows padded to whole 128-byte lines (MOE_FLAG_MX_LINE_ROWS; the
+    fraction still counts the codes' own bytes)."""
     import ctypes
     import numpy as np
     import torch
@@ -290,12 +296,21 @@ def time_mx_decode(Ts, iters, fmt="mxfp4"):
 
     cfg = NAMED["gpt_oss"]
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def tc(a):  # code rows, padded to whole lines with line_rows
+        if not line_rows:
+            return t(a)
+        R = a.shape[-1]
+        out = np.zeros(a.shape[:-1] + ((R + 127) // 128 * 128,), dtype=np.uint8)
+        out[..., :R] = a
+        return t(out)
+
     stack = generate.stacked_mxfp4 if fmt == "mxfp4" else generate.stacked_mxfp8
     u, us, g, gs, dn, ds = stack(cfg)
     li = tables.layer_inputs(cfg, max(Ts))
     W = moe.MxWeights(w_router=torch.from_numpy(li.w_router.view(np.int16)).view(torch.bfloat16).cuda(),
-                      up=t(u), up_scale=t(us), gate=t(g), gate_scale=t(gs), down=t(dn),
-                      down_scale=t(ds))
+                      up=tc(u), up_scale=t(us), gate=tc(g), gate_scale=t(gs), down=tc(dn),
+                      down_scale=t(ds), line_rows=line_rows, expert_format=fmt)
     del u, us, g, gs, dn, ds
     xall = torch.from_numpy(li.x.view(np.int16)).view(torch.bfloat16).cuda()
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")

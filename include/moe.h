@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -117,6 +117,20 @@ typedef enum moe_expert_format {
   MOE_EXPERTS_MXFP8 = 2
 } moe_expert_format;
 
+/*
+ * moe_desc.flags bits.
+ * MOE_FLAG_MX_LINE_ROWS (MXFP4 or MXFP8 experts only; MOE_ERR_INVALID_ARG
+ * with dense experts): every row of every code array (one weight row of K
+ * codes) starts on a 128-byte line, i.e. occupies ceil(K*bits/8 / 128) * 128
+ * bytes, its codes first; the bytes after them are never read.  Scale arrays
+ * keep their packed layout.  Results are identical to the packed layout's.
+ * It serves callers that can store the weights that way: whole-line rows
+ * let the expert kernels copy each row's codes without the second, partly
+ * used line that a row starting mid-line costs (the gpt-oss-shaped layer's
+ * 1440-byte MXFP4 rows: 4.5-7% faster).
+ */
+#define MOE_FLAG_MX_LINE_ROWS 1
+
 typedef struct moe_desc {
   int64_t T;          /* tokens, >= 0                                        */
   int32_t d;          /* hidden size                                         */
@@ -131,7 +145,7 @@ typedef struct moe_desc {
   int32_t scoring;    /* moe_scoring                                         */
   int32_t weighting;  /* moe_weighting                                       */
   int32_t expert_format; /* moe_expert_format                                */
-  int32_t flags;      /* reserved, must be 0                                 */
+  int32_t flags;      /* MOE_FLAG_* bits (0: none)                           */
   double capacity_factor; /* 0: dropless; > 0: expert capacity (see above)   */
 } moe_desc;
 
@@ -146,7 +160,8 @@ const char* moe_status_str(int status);
 
 /* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG (T<0, d/E/k/
  * ffn < 1, k > E, E > 512, k > 32, n_shared outside 0..8, ffn_shared < 1 with
- * n_shared > 0, bad enum, flags != 0, capacity_factor negative or not finite,
+ * n_shared > 0, bad enum, unknown flags or MOE_FLAG_MX_LINE_ROWS with dense
+ * experts, capacity_factor negative or not finite,
  * MXFP4 or MXFP8 experts with dtype MOE_F32, T*(k+n_shared) >= 2^31) or
  * MOE_ERR_UNSUPPORTED (MOE_BF16 with d, ffn or ffn_shared not a multiple of
  * 64, or with x (T*d), h ((T*(k+n_shared)+256)*max ffn) or one expert's
@@ -238,7 +253,9 @@ typedef struct moe_mx_scales {
  * [E,ffn,d/2], w_down [E,d,ffn/2] (and the shared counterparts) hold the
  * packed E2M1 codes, `scales` their E8M0 scales (16-byte aligned like the
  * codes).  With MOE_EXPERTS_MXFP8 the code arrays hold one E4M3 byte per
- * element: w_up, w_gate [E,ffn,d], w_down [E,d,ffn].  Every other argument
+ * element: w_up, w_gate [E,ffn,d], w_down [E,d,ffn].  With
+ * MOE_FLAG_MX_LINE_ROWS in desc->flags the last dimension of every code
+ * array is rounded up to a multiple of 128 bytes (rows on whole lines).  Every other argument
  * is as for moe_forward.  `events` is NULL or points to 6 hipEvents recorded as in
  * moe_forward_timed.  Scale bytes 0 (2^-127) and 255 (NaN) follow the format
  * but results that leave bfloat16's normal range are not defined.

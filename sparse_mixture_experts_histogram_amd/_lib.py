@@ -25,7 +25,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 WEIGHTS_RENORM, WEIGHTS_RAW = 0, 1
 EXPERTS_DENSE, EXPERTS_MXFP4, EXPERTS_MXFP8 = 0, 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
+FLAG_MX_LINE_ROWS = 1    # MOE_FLAG_MX_LINE_ROWS
 
 
 class MoeDesc(ctypes.Structure):

@@ -34,9 +34,10 @@ class Routing:
 def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
               dtype=torch.bfloat16, y_dtype=torch.float32, path: str = "auto",
               routing: Routing = Routing(), mxfp4: bool = False,
-              expert_format: Optional[str] = None) -> MoeDesc:
+              expert_format: Optional[str] = None, mx_line_rows: bool = False) -> MoeDesc:
     """Layer descriptor.  ``expert_format``: None / "dense", "mxfp4" or
-    "mxfp8" (``mxfp4=True`` is the same as "mxfp4")."""
+    "mxfp8" (``mxfp4=True`` is the same as "mxfp4").  ``mx_line_rows``: MX
+    code rows padded to whole 128-byte lines (MOE_FLAG_MX_LINE_ROWS)."""
     fmt = expert_format or ("mxfp4" if mxfp4 else "dense")
     return MoeDesc(T=T, d=d, E=E, k=k, ffn=ffn, n_shared=n_shared,
                    ffn_shared=ffn_shared if n_shared else 0, dtype=_DT[dtype],
@@ -44,7 +45,8 @@ def make_desc(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_s
                    weighting=_lib.WEIGHTS_RENORM if routing.renormalize else _lib.WEIGHTS_RAW,
                    expert_format={"dense": _lib.EXPERTS_DENSE, "mxfp4": _lib.EXPERTS_MXFP4,
                                   "mxfp8": _lib.EXPERTS_MXFP8}[fmt],
-                   flags=0, capacity_factor=float(routing.capacity_factor))
+                   flags=_lib.FLAG_MX_LINE_ROWS if mx_line_rows else 0,
+                   capacity_factor=float(routing.capacity_factor))
 
 
 def _check(status: int, where: str):
@@ -203,11 +205,19 @@ class MxWeights:
     s_gate_scale: Optional[torch.Tensor] = None
     s_down: Optional[torch.Tensor] = None
     s_down_scale: Optional[torch.Tensor] = None
+    # code rows padded to whole 128-byte lines: the code tensors' last
+    # dimension is the row's code bytes rounded up to a multiple of 128
+    line_rows: bool = False
+    # "mxfp4" or "mxfp8"; None: from the code tensors' last dimension (which
+    # is ambiguous only for padded rows of d <= 128)
+    expert_format: Optional[str] = None
 
     @property
     def format(self) -> str:
+        if self.expert_format is not None:
+            return self.expert_format
         d = self.up_scale.shape[2] * 32
-        return "mxfp8" if self.up.shape[2] == d else "mxfp4"
+        return "mxfp8" if self.up.shape[2] == _row_bytes(d, 1, self.line_rows) else "mxfp4"
 
     def desc(self, T: int, k: int, y_dtype=torch.float32,
              routing: Routing = Routing()) -> MoeDesc:
@@ -216,7 +226,14 @@ class MxWeights:
         ns = 0 if self.s_up is None else self.s_up.shape[0]
         fs = 0 if self.s_up is None else self.s_up.shape[1]
         return make_desc(T, d, E, k, ffn, ns, fs, torch.bfloat16, y_dtype, "auto",
-                         routing, expert_format=self.format)
+                         routing, expert_format=self.format, mx_line_rows=self.line_rows)
+
+
+def _row_bytes(K: int, per: int, line_rows: bool) -> int:
+    """Bytes of one code row of K codes, `per` codes per byte (rounded up to
+    whole 128-byte lines with line_rows)."""
+    n = K // per
+    return (n + 127) // 128 * 128 if line_rows else n
 
 
 def _check_mx(W: MxWeights, x: torch.Tensor):
@@ -225,7 +242,8 @@ def _check_mx(W: MxWeights, x: torch.Tensor):
     per = 2 if W.format == "mxfp4" else 1   # codes per byte
     if x.dtype != torch.bfloat16 or W.w_router.dtype != torch.bfloat16:
         raise ValueError("MX-format layers take bf16 x and router weight")
-    want = {"up": (E, ffn, d // per), "gate": (E, ffn, d // per), "down": (E, d, ffn // per),
+    rb = lambda K: _row_bytes(K, per, W.line_rows)
+    want = {"up": (E, ffn, rb(d)), "gate": (E, ffn, rb(d)), "down": (E, d, rb(ffn)),
             "up_scale": (E, ffn, d // 32), "gate_scale": (E, ffn, d // 32),
             "down_scale": (E, d, ffn // 32)}
     for name, shape in want.items():

@@ -64,6 +64,7 @@ struct GemmArgs {
   // kernel (see sk_layout).
   float* part;
   int sk_cus;
+  int mx_line;  // MX code rows padded to whole 128-byte lines (MOE_FLAG_MX_LINE_ROWS)
 };
 
 // Schedule of the last-round split.  `count` tiles on C workgroup slots run
@@ -884,7 +885,8 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
   const int K = sh ? a.K_s : a.K_r;
   if (tl.n0 >= N) return;
   const int ge = sh ? tl.g - a.E : tl.g;
-  const int64_t cstride = (int64_t)N * (K / 2), sstride = (int64_t)N * (K / 32);
+  const int rstr = a.mx_line ? (K / 2 + 127) & ~127 : K / 2;  // code row pitch, bytes
+  const int64_t cstride = (int64_t)N * rstr, sstride = (int64_t)N * (K / 32);
   const uint8_t* C[NS];
   const uint8_t* S[NS];
   C[0] = (const uint8_t*)(sh ? a.s0 : a.w0) + ge * cstride;
@@ -903,7 +905,7 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
     n = n < N ? n : N - 1;
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
-      cp[f][q] = C[q] + (int64_t)n * (K / 2) + g * 16;
+      cp[f][q] = C[q] + (int64_t)n * rstr + g * 16;
       sp[f][q] = S[q] + (int64_t)n * (K / 32) + g;
     }
   }
@@ -1063,7 +1065,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   const int nb = K >> 5;                 // 32-k blocks
   const int nst = (nb + 7) >> 3;         // 256-k stages
   const int rowb = K * EB / 8;           // code bytes per weight row
-  const int64_t cstride = (int64_t)N * rowb, sstride = (int64_t)N * nb;
+  const int rstr = a.mx_line ? (rowb + 127) & ~127 : rowb;  // row pitch in the code array
+  const int64_t cstride = (int64_t)N * rstr, sstride = (int64_t)N * nb;
   // one named array per stage, so the compiler tells reads of one stage
   // from copies still landing in another
   __shared__ __attribute__((aligned(1024))) uint16_t lx0[XS], lx1[XS], lx2[XS];
@@ -1109,7 +1112,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < NS; ++q)
       csrc[q][i] = (const uint8_t*)(q == 0 ? (sh ? a.s0 : a.w0) : (sh ? a.s1 : a.w1)) +
-                   ge * cstride + cn * rowb;
+                   ge * cstride + cn * rstr;
   }
   // the row lookups above have landed before any copy is issued (a load
   // into registers behind copies in flight would wait for all of them)
@@ -1349,7 +1352,8 @@ static GemmArgs up_args(const Plan& P, const ExpertArgs& x) {
                   (const uint16_t*)x.w_gate, (const uint16_t*)x.ws_up,
                   (const uint16_t*)x.ws_gate, D.E, D.ffn, ffn_s, D.d, D.d, x.h, P.ffn_max,
                   x.tiles_up, P.up.xcd_remap, 1, 0, (uint32_t)(D.T * D.d * 2),
-                  x.mx.up, x.mx.gate, x.mx.s_up, x.mx.s_gate, x.part, P.up.sk_cus};
+                  x.mx.up, x.mx.gate, x.mx.s_up, x.mx.s_gate, x.part, P.up.sk_cus,
+                  (D.flags & MOE_FLAG_MX_LINE_ROWS) ? 1 : 0};
 }
 static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
   const moe_desc& D = P.desc;
@@ -1359,7 +1363,8 @@ static GemmArgs down_args(const Plan& P, const ExpertArgs& x) {
                   x.tiles_down, P.down.xcd_remap, x.ksplit,
                   (int64_t)((size_t)P.R + kRowSlack) * D.d,
                   (uint32_t)(((size_t)P.R + kRowSlack) * P.ffn_max * 2), x.mx.down, nullptr,
-                  x.mx.s_down, nullptr, x.part, P.down.sk_cus};
+                  x.mx.s_down, nullptr, x.part, P.down.sk_cus,
+                  (D.flags & MOE_FLAG_MX_LINE_ROWS) ? 1 : 0};
 }
 
 // LDS stages (weights, tokens) of the prefill GEMM instantiations, at most

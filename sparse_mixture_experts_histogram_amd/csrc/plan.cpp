@@ -86,7 +86,9 @@ static int validate(const moe_desc* d) {
       d->expert_format != MOE_EXPERTS_MXFP8)
     return MOE_ERR_INVALID_ARG;
   if (d->expert_format != MOE_EXPERTS_DENSE && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (d->flags != 0) return MOE_ERR_INVALID_ARG;
+  if (d->flags & ~MOE_FLAG_MX_LINE_ROWS) return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_MX_LINE_ROWS) && d->expert_format == MOE_EXPERTS_DENSE)
+    return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d->capacity_factor) || d->capacity_factor < 0) return MOE_ERR_INVALID_ARG;
   const int64_t rows = d->T * (int64_t)(d->k + d->n_shared);
   if (rows + kRowSlack >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARG;

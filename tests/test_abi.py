@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
             "moe_workspace_size", "moe_validate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == _lib.ABI_VERSION == 4
+    assert L.moe_abi_version() == _lib.ABI_VERSION == 5
 
 
 def test_desc_struct_size():
@@ -47,7 +47,11 @@ def test_desc_struct_size():
     (dict(dtype=2), INVALID),
     (dict(y_dtype=5), INVALID),
     (dict(path=3), INVALID),
-    (dict(flags=1), INVALID),
+    (dict(flags=1), INVALID),                      # line rows with dense experts
+    (dict(flags=1, expert_format=1), OK),
+    (dict(flags=1, expert_format=2), OK),
+    (dict(flags=2, expert_format=1), INVALID),
+    (dict(flags=3, expert_format=2), INVALID),
     (dict(scoring=1), OK),
     (dict(scoring=2), INVALID),
     (dict(weighting=1), OK),

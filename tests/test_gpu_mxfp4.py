@@ -70,17 +70,31 @@ class MxCase:
                                   self.shared if c.n_shared else None, c.n_shared, tokens,
                                   expert_dtype=self.fmt)
 
-    def upload(self):
+    def upload(self, line_rows=False):
+        """Device tensors of the layer.  line_rows: code rows padded to whole
+        128-byte lines (MOE_FLAG_MX_LINE_ROWS), the padding filled with 0xFF
+        bytes (NaN codes in E4M3, -6 in E2M1: a kernel reading them would
+        change y)."""
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        tc = (lambda a: t(pad_rows(a))) if line_rows else t
         u, us, g, gs, d, ds = self.mx
-        W = moe.MxWeights(w_router=to_dev(self.w_router, "bf16"), up=t(u), up_scale=t(us),
-                          gate=t(g), gate_scale=t(gs), down=t(d), down_scale=t(ds),
-                          bias=None if self.bias is None else t(self.bias))
+        W = moe.MxWeights(w_router=to_dev(self.w_router, "bf16"), up=tc(u), up_scale=t(us),
+                          gate=tc(g), gate_scale=t(gs), down=tc(d), down_scale=t(ds),
+                          bias=None if self.bias is None else t(self.bias),
+                          line_rows=line_rows, expert_format=self.fmt)
         if self.smx is not None:
             su, sus, sg, sgs, sd, sds = self.smx
-            W.s_up, W.s_up_scale, W.s_gate, W.s_gate_scale = t(su), t(sus), t(sg), t(sgs)
-            W.s_down, W.s_down_scale = t(sd), t(sds)
+            W.s_up, W.s_up_scale, W.s_gate, W.s_gate_scale = tc(su), t(sus), tc(sg), t(sgs)
+            W.s_down, W.s_down_scale = tc(sd), t(sds)
         return to_dev(self.x, "bf16"), W
+
+
+def pad_rows(a: np.ndarray) -> np.ndarray:
+    """Code rows (last axis) padded with 0xFF bytes to a multiple of 128."""
+    R = a.shape[-1]
+    out = np.full(a.shape[:-1] + ((R + 127) // 128 * 128,), 0xFF, dtype=np.uint8)
+    out[..., :R] = a
+    return out
 
 
 @functools.lru_cache(maxsize=None)
@@ -234,3 +248,54 @@ def test_mxfp8_full_code_range():
     print(f"mxfp8 full code range: max|err|/rms = {rel_err(yg, ref.y):.3e}, "
           f"largest excess over the bound {excess.max() / rms:.2e} rms")
     assert excess.max() <= 1e-5 * rms, excess.max()
+
+
+def _same_layer(x, W0, W1, k):
+    y0, i0, w0, c0 = moe.moe_forward_mx(x, W0, k, return_routing=True)
+    y1, i1, w1, c1 = moe.moe_forward_mx(x, W1, k, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(w0, w1) and torch.equal(c0, c1)
+    assert torch.equal(y0, y1), float((y0 - y1).abs().max())
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_mx_line_rows_small(name, fmt):
+    """MX code rows padded to whole 128-byte lines give exactly the packed
+    layout's routing and y (both kernels, shared experts, partial tiles;
+    rows of 32 to 2048 code bytes, on and off line boundaries)."""
+    c = MxCase(SMALL[name], fmt=fmt)
+    x, W0 = c.upload()
+    _, W1 = c.upload(line_rows=True)
+    _same_layer(x, W0, W1, c.cfg.k)
+
+
+@functools.lru_cache(maxsize=None)
+def _gpt_oss_case(fmt):
+    cfg = NAMED["gpt_oss"]
+    li = tables.layer_inputs(cfg, 128)
+    return MxCase(cfg, 128, x=li.x, fmt=fmt)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_mx_line_rows_gpt_oss(fmt):
+    """The gpt-oss-shaped layer (rows of 1440 or 2880 code bytes, off line
+    boundaries) with line-padded code rows at T = 1, 8 and 128 (the MXFP4
+    direct-load kernel at T = 1, the LDS-staged one after): identical to the
+    packed layout."""
+    c = _gpt_oss_case(fmt)
+    x, W0 = c.upload()
+    _, W1 = c.upload(line_rows=True)
+    for T in (1, 8, 128):
+        _same_layer(x[:T].contiguous(), W0, W1, c.cfg.k)
+    del W0, W1
+    torch.cuda.empty_cache()
+
+
+def test_mx_line_rows_desc_flag():
+    """The flag rides in the descriptor only for padded layers."""
+    c = case_of("mx_ragged")
+    _, W0 = c.upload()
+    _, W1 = c.upload(line_rows=True)
+    assert W0.desc(8, 2).flags == 0
+    assert W1.desc(8, 2).flags == moe._lib.FLAG_MX_LINE_ROWS
