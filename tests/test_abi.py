@@ -162,3 +162,32 @@ def test_noalloc_host_checks():
     small = desc(T=512, d=2880, E=128, k=4, ffn=2880)
     assert L.moe_workspace_size(small, ctypes.byref(n)) == OK
     assert n.value <= _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_mx_line_rows_host_logic():
+    """Host side of MOE_FLAG_MX_LINE_ROWS (no GPU): code-row bytes rounded up
+    to whole 128-byte lines, the format read from padded code tensors, an
+    explicit format where padding makes it ambiguous, and the flag in the
+    descriptor."""
+    import torch
+    from sparse_mixture_experts_histogram_amd import api
+    assert api._row_bytes(2880, 2, False) == 1440
+    assert api._row_bytes(2880, 2, True) == 1536
+    assert api._row_bytes(2880, 1, True) == 2944
+    assert api._row_bytes(4096, 2, True) == 2048   # already whole lines
+    assert api._row_bytes(64, 2, True) == 128
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8)
+    def mxw(code_bytes, d=2880, **kw):
+        return api.MxWeights(w_router=torch.empty((4, d), dtype=torch.bfloat16),
+                             up=u8(4, 64, code_bytes), up_scale=u8(4, 64, d // 32),
+                             gate=u8(4, 64, code_bytes), gate_scale=u8(4, 64, d // 32),
+                             down=u8(4, d, 32), down_scale=u8(4, d, 2), **kw)
+    assert mxw(1440).format == "mxfp4" and mxw(2880).format == "mxfp8"
+    assert mxw(1536, line_rows=True).format == "mxfp4"
+    assert mxw(2944, line_rows=True).format == "mxfp8"
+    # d = 128: padded FP4 and FP8 rows are both 128 bytes; the explicit format decides
+    assert mxw(128, d=128, line_rows=True, expert_format="mxfp4").format == "mxfp4"
+    assert mxw(1536, line_rows=True).desc(8, 2).flags == _lib.FLAG_MX_LINE_ROWS
+    assert mxw(1440).desc(8, 2).flags == 0
+    L = _lib.lib()
+    assert L.moe_validate(ctypes.byref(mxw(1536, line_rows=True).desc(8, 2))) == 0
