@@ -1037,8 +1037,12 @@ __global__ __launch_bounds__(256) void gemm_mx_stream_kernel(GemmArgs a) {
 // non-temporally it was fetched twice.  Measured on MI355X, gpt-oss-shaped
 // FP4 layer, T=128: L2 fetch of the up/gate GEMM 1.66x -> 1.11x the code and
 // scale bytes, layer 0.487 -> 0.432 ms (T=32 and T=512 also -10%; FP8 -1%).
-constexpr int kMxCodePolicy = 0;
-template <bool UPGATE, int NW, int EB>
+// CPOL is that policy: 0, or non-temporal (kWeightPolicy) for code rows on
+// whole lines (MOE_FLAG_MX_LINE_ROWS) when about one row tile reads each
+// weight tile (measured, gpt-oss-shaped line-row layer: T = 8 ... 128 -3 to
+// -5% for both formats; T=512, where experts of more than 16 rows read
+// their codes twice, +5 to +9%, so it keeps the default there).
+template <bool UPGATE, int NW, int EB, int CPOL = 0>
 __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
   constexpr int NS = UPGATE ? 2 : 1;
   constexpr int XS = 16 * 256;               // token stage, bf16 elements (8 KB)
@@ -1153,7 +1157,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_lds_kernel(GemmArgs a) {
         b = b < rowb / 16 ? b : rowb / 16 - 1;
         __builtin_amdgcn_global_load_lds((const void*)(csrc[q][i] + b * 16),
                                          LDS_PTR(lc + (wave * NS + q) * 16 * RB + i * 1024), 16,
-                                         0, kMxCodePolicy);
+                                         0, CPOL);
       }
   };
   f32x4 acc[NS];
@@ -1408,9 +1412,15 @@ hipError_t launch_expert_up(const Plan& P, const ExpertArgs& x, hipStream_t s) {
     hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, block, 0, s, u);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP8)
+  if (P.kind == KIND_MXFP8 && P.up.stream_w)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMx8Waves, 8, kWeightPolicy>), grid,
+                       dim3(64 * kMx8Waves), 0, s, up_args(P, x));
+  else if (P.kind == KIND_MXFP8)
     hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMx8Waves, 8>), grid, dim3(64 * kMx8Waves), 0, s,
                        up_args(P, x));
+  else if (P.kind == KIND_MXFP4 && P.up.bn == 16 * kMxUpWaves && P.up.stream_w)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMxUpWaves, 4, kWeightPolicy>), grid,
+                       dim3(64 * kMxUpWaves), 0, s, up_args(P, x));
   else if (P.kind == KIND_MXFP4 && P.up.bn == 16 * kMxUpWaves)
     hipLaunchKernelGGL((gemm_mx_lds_kernel<true, kMxUpWaves, 4>), grid, dim3(64 * kMxUpWaves), 0,
                        s, up_args(P, x));
@@ -1441,9 +1451,15 @@ hipError_t launch_expert_down(const Plan& P, const ExpertArgs& x, hipStream_t s)
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, block, 0, s, dn);
     return hipGetLastError();
   }
-  if (P.kind == KIND_MXFP8)
+  if (P.kind == KIND_MXFP8 && P.down.stream_w)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMx8Waves, 8, kWeightPolicy>), grid,
+                       dim3(64 * kMx8Waves), 0, s, down_args(P, x));
+  else if (P.kind == KIND_MXFP8)
     hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMx8Waves, 8>), grid, dim3(64 * kMx8Waves), 0, s,
                        down_args(P, x));
+  else if (P.kind == KIND_MXFP4 && P.down.bn == 16 * kMxDownWaves && P.down.stream_w)
+    hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMxDownWaves, 4, kWeightPolicy>), grid,
+                       dim3(64 * kMxDownWaves), 0, s, down_args(P, x));
   else if (P.kind == KIND_MXFP4 && P.down.bn == 16 * kMxDownWaves)
     hipLaunchKernelGGL((gemm_mx_lds_kernel<false, kMxDownWaves, 4>), grid, dim3(64 * kMxDownWaves),
                        0, s, down_args(P, x));

@@ -233,6 +233,12 @@ int make_plan(const moe_desc* d, Plan* p) {
   P.up.stream_w = P.down.stream_w = 0;
   if (P.kind == KIND_BF16_PREFILL && P.up.bm <= 128 && P.pairs * 4 <= (int64_t)P.up.bm * d->E)
     P.up.stream_w = P.down.stream_w = 1;
+  // MX code copies of the LDS-staged kernel go non-temporal for code rows on
+  // whole lines with at most 8 (token, expert) pairs per expert on average
+  // (each weight tile then read by about one 16-row tile; see experts.hip).
+  if ((P.kind == KIND_MXFP4 || P.kind == KIND_MXFP8) && (d->flags & MOE_FLAG_MX_LINE_ROWS) &&
+      P.pairs <= 8LL * d->E)
+    P.up.stream_w = P.down.stream_w = 1;
   // A split down GEMM measured faster with its entries spread over all XCDs.
   if (P.down.ksplit > 1) P.down.xcd_remap = 0;
 

@@ -57,7 +57,8 @@ struct GemmShape {
   int n_fastest;          // within a schedule chunk: 0 = row tile fastest, 1 = column
   int xcd_remap;          // consecutive schedule entries on one XCD (1) or spread (0)
   int ksplit;             // K ranges per tile in moe_forward (down GEMM only)
-  int stream_w;           // weight bursts non-temporal (prefill kernels, 64- and 128-row tiles)
+  int stream_w;           // weight bursts non-temporal (prefill kernels, 64- and 128-row
+                          // tiles; MX LDS-staged kernel with line-row codes)
   int sk_cus;             // last-round split over this many workgroup slots (0: off)
   int all_rows;           // 256-row tiles whose waves each span all rows (prefill)
 };
